@@ -1,0 +1,304 @@
+"""CPU oracle for the forward pass of the sparse MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or execute
+this module: only the tests, the smoke check and the bench's CPU-baseline leg do.  It
+shares no code with the HIP library and imports nothing from it.
+
+It is a plain, slow, obviously correct numpy implementation written from the pages:
+
+  [book ch.30]   "Chapter 30: Mixture of Experts", LLM Transformer book, Japanese
+                 edition (waylandz.com)
+  [MoE guide]    "Mixture of Experts guide" (ai-native-b2y.pages.dev)
+  [MoE memo]     "Mixture of Experts (MoE) memo" (iwashi.co)
+  [MoE practice] "Mixture-of-experts in practice: routing, load balancing and parallel
+                 configuration" (deepseekmodel.com blog)
+
+Precision.  Inputs arrive as float32 arrays holding bf16 (or fp32) values and are
+widened exactly to float64.  Every dot product and reduction runs in float64 and is
+rounded once to float32 where the layer has a float32 boundary: the router
+probabilities, the selection score, the mixing weights, the expert intermediate h
+(rounded further to bf16 for the bf16 workloads, because h is the down projection's
+input) and the expert output o.  Decisions that floating point makes for an integer
+(the top-k choice) are taken in float32, the precision the layer computes them in.
+
+Readings where the pages are silent or disagree (each one is listed in the design
+notes of the repository):
+  * the selection bias is added to the softmax probabilities, not the logits;
+  * ties in the selection score go to the lower expert index, and slots are ordered
+    by selection score, highest first;
+  * f_e counts top-k assignments before any capacity drop and is normalised by T*k;
+  * capacity C = max(floor(cf * k * T / E), k); assignments are ranked per expert in
+    row-major (token, slot) order and the first C are kept;
+  * a dropped assignment contributes zero; the layer adds no residual.
+
+Pins: tests/test_oracle_pins.py checks each function against values the pages print,
+closed forms, library routines and brute force.  Large-shape absolute values are
+"parity unpinned" except through these functions.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------- numerics
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16, ties to even; returns float32.
+
+    bfloat16 keeps the top 16 bits of an IEEE float32.  Round-to-nearest-even adds
+    0x7FFF plus the lowest kept bit, then truncates.  Inputs are finite here.
+    """
+    u = np.ascontiguousarray(a, dtype=F32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(F32)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))   ([book ch.30] 30.2.4)."""
+    return z / (1.0 + np.exp(-z))
+
+
+# ----------------------------------------------------------------------------- router
+def router_probs(x: np.ndarray, W_router: np.ndarray) -> np.ndarray:
+    """Router linear layer without bias, then softmax over the experts.
+
+    logits[t, e] = sum_i x[t, i] * W_router[e, i]     ([book ch.30] 30.2.3 step 1;
+    [MoE practice] routing-math section: the gate is a bias-free linear layer)
+    p[t, :] = softmax(logits[t, :])                   ([book ch.30] 30.2.3 step 2)
+    Computed in float64, returned rounded to float32.
+    """
+    logits = x.astype(F64) @ W_router.astype(F64).T
+    z = logits - logits.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=1, keepdims=True)).astype(F32)
+
+
+def select_topk(p: np.ndarray, k: int, bias: np.ndarray | None = None):
+    """Top-k expert choice on the selection score s = p + bias.
+
+    [book ch.30] 30.2.3 step 3 picks the k largest probabilities; with the
+    aux-loss-free bias ([MoE memo] DeepSeek-V3 section; [MoE practice] load-balancing
+    section, bias-balanced router) the bias enters the choice only.  s is formed in
+    float32.  Order: s descending, ties to the lower expert index.
+
+    Returns (idx [T,k] int32, s [T,E] float32, margin [T] float64) where margin is the
+    smallest difference between neighbouring scores among the first k+1 in sorted
+    order (the k-th/(k+1)-th gap, and the gaps that fix the order of the k slots);
+    +inf when k == E == 1.
+    """
+    T, E = p.shape
+    s = p.astype(F32) if bias is None else (p.astype(F32) + bias.astype(F32)[None, :])
+    s = s.astype(F32)
+    # stable sort on (-s) keeps the lower index first among equal scores
+    order = np.argsort(-s.astype(F64), axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    m = min(k + 1, E)
+    srt = np.take_along_axis(s, order[:, :m], axis=1).astype(F64)
+    if m >= 2:
+        margin = (srt[:, :-1] - srt[:, 1:]).min(axis=1)
+    else:
+        margin = np.full(T, np.inf)
+    return idx, s, margin
+
+
+def renorm_weights(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]] / sum_j' p[t, idx[t, j']] on the unbiased probabilities.
+
+    [book ch.30] 30.2.3 step 4; [MoE practice] routing-math section (renormalise
+    always) and bias-balanced router (weights from the raw distribution).
+    """
+    sel = np.take_along_axis(p.astype(F64), idx.astype(np.int64), axis=1)
+    return (sel / sel.sum(axis=1, keepdims=True)).astype(F32)
+
+
+def route(x, W_router, k, bias=None):
+    """Router + top-k + renorm.  Returns dict(p, idx, w, s, margin)."""
+    p = router_probs(x, W_router)
+    idx, s, margin = select_topk(p, k, bias)
+    w = renorm_weights(p, idx)
+    return {"p": p, "idx": idx, "w": w, "s": s, "margin": margin}
+
+
+def aux_stats(p: np.ndarray, idx: np.ndarray, E: int):
+    """Switch-style statistics f and P.
+
+    f_e = share of the T*k top-k assignments that went to expert e (before capacity)
+    P_e = mean over tokens of the router probability of expert e
+    ([MoE memo] auxiliary-loss section, worked 2-expert example; [book ch.30] 30.2.6;
+    [MoE practice] load-balancing section).  The loss itself is E * sum_e f_e * P_e.
+    """
+    T, k = idx.shape
+    counts = np.bincount(idx.ravel().astype(np.int64), minlength=E)
+    f = (counts.astype(F64) / float(T * k)).astype(F32)
+    P = p.astype(F64).mean(axis=0).astype(F32)
+    return f, P
+
+
+def balance_loss(f, P) -> float:
+    """E * sum_e f_e * P_e; equals 1 under uniform routing ([MoE memo] aux-loss section)."""
+    return float(len(f) * np.sum(np.asarray(f, F64) * np.asarray(P, F64)))
+
+
+# ----------------------------------------------------------------------------- dispatch
+def capacity(T: int, k: int, E: int, cf: float):
+    """Per-expert capacity C = max(floor(cf * k * T / E), k); None when cf <= 0.
+
+    [MoE practice] routing-math section (capacity from the expected load, at least k);
+    [book ch.30] 30.5.2 and [MoE guide] expert-capacity section give (T/E)*cf, the same
+    number for top-1.
+    """
+    if cf is None or cf <= 0:
+        return None
+    return max(int(math.floor(cf * k * T / E)), k)
+
+
+def dispatch(idx: np.ndarray, E: int, C=None):
+    """Group the (token, slot) assignments by expert, stably, with the capacity cut.
+
+    The T*k assignments are flattened row-major (i = t*k + j) and stably sorted by
+    expert id ([MoE practice] expert-parallel section: flatten, stable argsort,
+    bincount).  The r-th assignment of expert e in that order has rank r; it is kept
+    iff r < C.  Kept rows of expert e occupy [offsets[e], offsets[e+1]).
+
+    Returns dict(counts [E], kept [E], offsets [E+1], perm_src [N], slot_pos [T*k]):
+    perm_src[pos] = i of the assignment in row pos; slot_pos[i] = pos or -1 (dropped).
+    """
+    flat = idx.reshape(-1).astype(np.int64)
+    n = flat.size
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    start = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rank = np.empty(n, np.int64)
+    rank[order] = np.arange(n) - start[flat[order]]
+    kept = counts if C is None else np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    keep = np.ones(n, bool) if C is None else rank < C
+    slot_pos = np.where(keep, offsets[flat] + rank, -1)
+    perm_src = np.empty(int(offsets[-1]), np.int64)
+    perm_src[slot_pos[keep]] = np.nonzero(keep)[0]
+    return {
+        "counts": counts.astype(np.int32), "kept": kept.astype(np.int32),
+        "offsets": offsets.astype(np.int32), "perm_src": perm_src.astype(np.int32),
+        "slot_pos": slot_pos.astype(np.int32),
+    }
+
+
+# ----------------------------------------------------------------------------- experts
+def expert_ffn(x_rows, Wg, Wu, Wd, h_bf16: bool) -> np.ndarray:
+    """One SwiGLU expert on a block of rows: o = W2( SiLU(W1 x) * W3 x ).
+
+    [book ch.30] 30.2.4 and 30.6.1: w1 (gate) goes through SiLU, w3 (up) is linear,
+    w2 (down) projects back; no biases.  Here Wg = w1 [F,d], Wu = w3 [F,d],
+    Wd = w2 [d,F].  h = fp32(SiLU(g) * u), rounded to bf16 when the layer's
+    activations are bf16; o = fp32(W2 h).
+    """
+    xr = np.asarray(x_rows, F64)
+    g = xr @ np.asarray(Wg, F64).T
+    u = xr @ np.asarray(Wu, F64).T
+    h = (silu(g) * u).astype(F32)
+    if h_bf16:
+        h = bf16_round(h)
+    return (h.astype(F64) @ np.asarray(Wd, F64).T).astype(F32)
+
+
+def combine(T, d, w, slot_pos, Y, shared=None) -> np.ndarray:
+    """y[t] = sum over kept slots j (ascending) of w[t,j] * Y[slot_pos[t,j]] (+ shared[t]).
+
+    [book ch.30] 30.6.1 (weighted accumulation per token); a dropped slot contributes
+    zero ([MoE practice] capacity section: the FFN branch of a dropped token is 0);
+    the shared expert is added with weight 1 ([book ch.30] 30.4.5).  float64 sums,
+    rounded to float32.
+    """
+    k = w.shape[1]
+    y = np.zeros((T, d), F64)
+    sp = slot_pos.reshape(T, k)
+    for j in range(k):
+        rows = np.nonzero(sp[:, j] >= 0)[0]
+        y[rows] += w[rows, j].astype(F64)[:, None] * Y[sp[rows, j]].astype(F64)
+    if shared is not None:
+        y += shared.astype(F64)
+    return y.astype(F32)
+
+
+# ----------------------------------------------------------------------------- layer
+def _np(a):
+    """torch tensor or array -> float32 numpy array (bf16 widens exactly)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        import torch
+        return a.detach().to("cpu", torch.float32).numpy()
+    return np.asarray(a, F32)
+
+
+def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
+            h_bf16: bool = True, idx_override=None) -> dict:
+    """The whole layer: route -> stats -> dispatch -> grouped experts -> combine.
+
+    ``inputs`` holds x, W_router, router_bias (or None), W_gate, W_up, W_down as torch
+    tensors or float32 arrays.  ``idx_override`` replaces the top-k choice (used where
+    near-tied tokens have more than one correct routing); the weights are then
+    renormalised from the same unbiased probabilities.
+    """
+    x = _np(inputs["x"])
+    Wr = _np(inputs["W_router"])
+    b = _np(inputs.get("router_bias"))
+    T, d = x.shape
+    E = Wr.shape[0]
+    r = route(x, Wr, k, b)
+    if idx_override is not None:
+        r["idx"] = np.asarray(idx_override, np.int32)
+        r["w"] = renorm_weights(r["p"], r["idx"])
+    f, P = aux_stats(r["p"], r["idx"], E)
+    C = capacity(T, k, E, capacity_factor)
+    disp = dispatch(r["idx"], E, C)
+    Y = np.zeros((int(disp["offsets"][-1]), d), F32)
+    for e in range(E):
+        lo, hi = int(disp["offsets"][e]), int(disp["offsets"][e + 1])
+        if hi == lo:
+            continue
+        tok = disp["perm_src"][lo:hi] // k
+        Y[lo:hi] = expert_ffn(x[tok], _np(inputs["W_gate"][e]), _np(inputs["W_up"][e]),
+                              _np(inputs["W_down"][e]), h_bf16)
+    shared = None
+    if n_shared:
+        shared = expert_ffn(x, _np(inputs["W_gate"][E]), _np(inputs["W_up"][E]),
+                            _np(inputs["W_down"][E]), h_bf16)
+    y = combine(T, d, r["w"], disp["slot_pos"], Y, shared)
+    return {"y": y, "f": f, "p": P, "route": r, "dispatch": disp, "C": C}
+
+
+def forward_rows(inputs: dict, rows, k: int, capacity_factor: float = 0.0,
+                 n_shared: int = 0, h_bf16: bool = True, routing: dict | None = None,
+                 disp: dict | None = None) -> np.ndarray:
+    """Output rows y[rows] of the whole layer, computing experts only for those rows.
+
+    Routing and dispatch (which decide drops under a capacity) are computed for every
+    token, exactly as in ``forward``; the expert FFNs run only for the requested
+    tokens.  Used where the full layer is too large for the CPU.
+    """
+    x = _np(inputs["x"])
+    T, d = x.shape
+    if routing is None:
+        routing = route(x, _np(inputs["W_router"]), k, _np(inputs.get("router_bias")))
+    E = routing["p"].shape[1]
+    if disp is None:
+        disp = dispatch(routing["idx"], E, capacity(T, k, E, capacity_factor))
+    rows = np.asarray(rows, np.int64)
+    sp = disp["slot_pos"].reshape(T, k)[rows]
+    idx = routing["idx"][rows]
+    w = routing["w"][rows]
+    y = np.zeros((rows.size, d), F64)
+    for e in np.unique(idx[sp >= 0]):
+        sel = np.argwhere((idx == e) & (sp >= 0))        # (row-in-sample, slot)
+        o = expert_ffn(x[rows[sel[:, 0]]], _np(inputs["W_gate"][e]),
+                       _np(inputs["W_up"][e]), _np(inputs["W_down"][e]), h_bf16)
+        y[sel[:, 0]] += w[sel[:, 0], sel[:, 1]].astype(F64)[:, None] * o.astype(F64)
+    if n_shared:
+        y += expert_ffn(x[rows], _np(inputs["W_gate"][E]), _np(inputs["W_up"][E]),
+                        _np(inputs["W_down"][E]), h_bf16).astype(F64)
+    return y.astype(F32)

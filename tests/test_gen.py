@@ -1,0 +1,64 @@
+"""The seeded input generator: determinism, shapes, dtypes and the load structure of
+each synthetic workload (checked with the oracle's router on the CPU)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+
+
+def test_deterministic_and_thread_independent():
+    wl = gen.workload("tiny_f32")
+    a = gen.make_inputs(wl, seed=3, threads=1)
+    b = gen.make_inputs(wl, seed=3, threads=4)
+    for key in gen.ALL_PARTS:
+        if a[key] is None:
+            assert b[key] is None
+            continue
+        assert torch.equal(a[key], b[key])
+    c = gen.make_inputs(wl, seed=4)
+    assert not torch.equal(a["x"], c["x"])
+    part = gen.make_inputs(wl, seed=3, parts=("W_up",))
+    assert torch.equal(part["W_up"], a["W_up"]) and "x" not in part
+
+
+def test_shapes_dtypes_and_scales():
+    wl = gen.workload("fine_grained_shared").replace(T=40, d=128, E=16, F=64)
+    inp = gen.make_inputs(wl)
+    assert inp["x"].shape == (40, 128) and inp["x"].dtype == torch.bfloat16
+    assert inp["W_gate"].shape == (17, 64, 128) and inp["W_down"].shape == (17, 128, 64)
+    assert inp["router_bias"].dtype == torch.float32
+    b = inp["router_bias"]
+    assert float(b.abs().max()) <= 0.1 and float(b.min()) < 0 < float(b.max())
+    # N(0, 1/fan_in): sample std within a few percent
+    assert abs(float(inp["W_up"].float().std()) * np.sqrt(128) - 1) < 0.05
+    assert abs(float(inp["W_down"].float().std()) * np.sqrt(64) - 1) < 0.05
+
+
+def _loads(name, T=None):
+    wl = gen.workload(name)
+    if T:
+        wl = wl.replace(T=T)
+    inp = gen.make_inputs(wl, parts=("x", "W_router", "router_bias"))
+    r = oracle.route(oracle.moe_oracle._np(inp["x"]), oracle.moe_oracle._np(inp["W_router"]),
+                     wl.k, oracle.moe_oracle._np(inp["router_bias"]))
+    return np.bincount(r["idx"].ravel(), minlength=wl.E), wl
+
+
+def test_prefill_loads_are_skewed_about_3_to_1():
+    c, _ = _loads("mixtral_prefill")
+    assert c.sum() == 4096 * 2
+    assert 2.5 <= c.max() / c.min() <= 3.6, c
+
+
+def test_switch_loads_follow_zipf_and_capacity_drops():
+    c, wl = _loads("switch_capacity")
+    C = oracle.capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    assert C == 320
+    share = c / c.sum()
+    pi = (np.arange(64) + 1.0) ** -1.1
+    pi /= pi.sum()
+    assert abs(share[0] - pi[0]) < 0.03
+    kept = np.minimum(c, C).sum()
+    assert 0.40 < 1 - kept / c.sum() < 0.60     # about half of the tokens overflow
