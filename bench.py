@@ -1,0 +1,246 @@
+"""Throughput of the MoE-layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_prefill]
+
+One step = one moe_forward over one batch of synthetic tokens (router, top-k, dispatch,
+grouped SwiGLU experts, combine, f/P statistics), inputs resident in HBM.  Prints ONE
+JSON line (stdout).  Besides the whole-layer rate it times each stage with HIP events on
+the launch stream (staged entry points, same kernels) to report the dominant kernel
+against its roofline, and times the CPU oracle on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # fp32 vector
+PEAK_HBM_GBS = 8000.0         # HBM3E
+# Which roof bounds the dominant (gate/up) kernel for each workload.
+BOUND = {"mixtral_prefill": "mfma", "fine_grained_shared": "mfma", "mixtral_decode": "hbm",
+         "switch_capacity": "hbm", "tiny_f32": "alu"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this layer is built and timed on a single "
+              "MI355X (no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import sparse_mixture_experts_24_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = gen.workload(args.workload)
+    log(f"[bench] workload {wl.name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F} "
+        f"S={wl.n_shared} cf={wl.capacity_factor} dtype={wl.dtype}")
+    t0 = time.time()
+    inp = gen.make_inputs(wl, seed=0)
+    dinp = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    torch.cuda.synchronize()
+    log(f"[bench] inputs drawn and resident in HBM ({time.time() - t0:.1f}s)")
+
+    T, d, E, k, F, S = wl.T, wl.d, wl.E, wl.k, wl.F, wl.n_shared
+    out_dtype = wl.torch_dtype
+    desc = moe.desc_for(dinp["x"], dinp["W_router"], dinp["W_gate"], k, wl.capacity_factor,
+                        out_dtype)
+    ws = moe.alloc_workspace(desc, dev)
+    out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    p = torch.empty(E, dtype=torch.float32, device=dev)
+    L = moe.lib()
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    dref = ctypes.byref(desc)
+    fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]),
+                P(dinp["W_gate"]), P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p),
+                P(ws), ws.numel(), sp)
+
+    def step():
+        st = L.moe_forward(*fwd_args)
+        if st:
+            raise moe.MoeError("moe_forward", st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] moe_forward: {ms:.4f} ms/step (events), wall {1e3 * wall / args.steps:.4f} ms/step")
+
+    # ---- staged: the same kernels through the stage entry points, events between them
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+    rows = T * k + S * T
+    H = torch.empty(rows, F, dtype=wl.torch_dtype, device=dev)
+    Yp = torch.empty(rows, d, dtype=torch.float32, device=dev)
+    out2 = torch.empty_like(out)
+    calls = [
+        ("route", lambda: L.moe_route(dref, P(dinp["x"]), P(dinp["W_router"]),
+                                      P(dinp["router_bias"]), P(idx), P(w), P(f), P(p), P(ws),
+                                      ws.numel(), sp)),
+        ("dispatch", lambda: L.moe_dispatch(dref, P(idx), P(counts), P(offsets), P(perm),
+                                            P(slot), P(ws), ws.numel(), sp)),
+        ("gate_up", lambda: L.moe_experts_gate_up(dref, P(dinp["x"]), P(perm), P(offsets),
+                                                  P(dinp["W_gate"]), P(dinp["W_up"]), P(H), sp)),
+        ("down", lambda: L.moe_experts_down(dref, P(H), P(offsets), P(dinp["W_down"]), P(Yp), sp)),
+        ("combine", lambda: L.moe_combine(dref, P(Yp), P(slot), P(w), P(out2), sp)),
+    ]
+    for _ in range(max(1, args.warmup)):
+        for name, c in calls:
+            if c():
+                raise RuntimeError(f"staged {name} failed")
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, (name, c) in enumerate(calls):
+            if c():
+                raise RuntimeError(f"staged {name} failed")
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
+                                     for s in range(args.steps)]))
+                for i, (name, _) in enumerate(calls)}
+    log("[bench] stages (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in stage_ms.items()))
+    same = torch.equal(out, out2)
+    log(f"[bench] staged output identical to moe_forward: {same}")
+
+    # ---- realised routing -> algorithmic work
+    cnt = counts.cpu().numpy().astype(np.int64)
+    offs = offsets.cpu().numpy().astype(np.int64)
+    kept = np.diff(offs)
+    N = int(offs[-1])
+    touched = int(np.count_nonzero(kept)) + S
+    esz = 2 if wl.dtype == "bf16" else 4
+    flops_gate_up = 4.0 * d * F * (N + S * T)
+    flops_down = 2.0 * d * F * (N + S * T)
+    flops_layer = 2.0 * T * d * E + flops_gate_up + flops_down
+    w_gate_up_bytes = touched * 2.0 * F * d * esz
+    bytes_gate_up = w_gate_up_bytes + T * d * esz + (N + S * T) * F * esz
+    bytes_layer = touched * 3.0 * F * d * esz + E * d * esz + T * d * esz + T * d * esz
+    log(f"[bench] counts per expert: {cnt.tolist() if E <= 64 else (cnt.min(), cnt.max())}; "
+        f"kept N={N} of {T * k}; experts touched {touched}")
+
+    gu_s = stage_ms["gate_up"] / 1e3
+    bound = BOUND.get(wl.name, "mfma")
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": flops_gate_up / gu_s / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    elif bound == "hbm":
+        roof = {"bound": "hbm", "achieved": bytes_gate_up / gu_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "alu", "achieved": flops_gate_up / gu_s / 1e12,
+                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_bf16_kernel<true> (gate/up + SiLU*mul)" if wl.dtype == "bf16" else \
+        "gemm_f32_kernel<true>"
+    roof["kernel_ms"] = stage_ms["gate_up"]
+    roof["algorithmic_per_launch"] = flops_gate_up if bound != "hbm" else bytes_gate_up
+
+    layer_s = ms / 1e3
+    layer = {
+        "tflops": flops_layer / layer_s / 1e12,
+        "mfma_frac": flops_layer / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+        "gbs": bytes_layer / layer_s / 1e9,
+        "hbm_frac": bytes_layer / layer_s / 1e9 / PEAK_HBM_GBS,
+        "flops": flops_layer, "bytes": bytes_layer, "kept_assignments": N,
+        "experts_touched": touched, "stage_ms": stage_ms,
+    }
+
+    # ---- CPU oracle on a bounded sample of the same batch
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_sample)
+
+    rec = {
+        "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; shapes and load structure of the workload)",
+        "config": {"workload": wl.name, "T": T, "d_model": d, "n_experts": E, "top_k": k,
+                   "d_ff": F, "n_shared": S, "capacity_factor": wl.capacity_factor,
+                   "selection_bias": wl.bias_range > 0, "out_dtype": str(out_dtype).split(".")[-1]},
+        "roofline": roof,
+        "layer": layer,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, inp, sample):
+    """The oracle, as it stands, on the host cores: routing + dispatch of the whole batch
+    plus the experts of a sample of tokens, scaled to the whole batch."""
+    import numpy as np
+
+    import oracle
+    from oracle import moe_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    if not sample:
+        per_tok = 6.0 * wl.d * wl.F * (wl.k + wl.n_shared)
+        sample = int(max(8, min(wl.T, 1.0e12 / per_tok)))
+    t0 = time.perf_counter()
+    x = mo._np(inp["x"])
+    r = oracle.route(x, mo._np(inp["W_router"]), wl.k, mo._np(inp["router_bias"]))
+    C = oracle.capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    disp = oracle.dispatch(r["idx"], wl.E, C)
+    oracle.aux_stats(r["p"], r["idx"], wl.E)
+    t_route = time.perf_counter() - t0
+    rows = np.linspace(0, wl.T - 1, sample).astype(np.int64)
+    t1 = time.perf_counter()
+    oracle.forward_rows(inp, rows, wl.k, wl.capacity_factor, wl.n_shared,
+                        h_bf16=(wl.dtype == "bf16"), routing=r, disp=disp)
+    t_exp = time.perf_counter() - t1
+    full = t_route + t_exp * wl.T / rows.size
+    log(f"[bench] oracle: route+dispatch {t_route:.2f}s for {wl.T} tokens, experts "
+        f"{t_exp:.2f}s for {rows.size} tokens -> {full:.1f}s per batch")
+    return {"value": wl.T / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"routing+dispatch of all {wl.T} tokens ({t_route:.2f}s) + experts of "
+                      f"{rows.size} evenly spaced tokens ({t_exp:.2f}s), scaled to the batch"}
+
+
+if __name__ == "__main__":
+    main()

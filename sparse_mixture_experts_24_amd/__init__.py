@@ -1,0 +1,316 @@
+"""MI355X (gfx950) sparse mixture-of-experts FFN forward pass.
+
+Thin ctypes binding over libmoe.so (C ABI in include/moe.h).  PyTorch supplies device
+memory and the current HIP stream; every step of the layer runs in the library's HIP
+kernels.  The functions mirror the C entry points:
+
+    forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor, ...)
+    route(...), dispatch(...), experts(...), combine(...)
+
+There is no fallback: without the built library (python -m
+sparse_mixture_experts_24_amd.build) every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_UNSUPPORTED",
+          4: "MOE_E_WORKSPACE", 5: "MOE_E_HIP"}
+EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_capacity",
+           "moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_experts_gate_up",
+           "moe_experts_down", "moe_combine")
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("d_model", ctypes.c_int64), ("n_experts", ctypes.c_int64),
+        ("d_ff", ctypes.c_int64), ("top_k", ctypes.c_int64), ("n_shared", ctypes.c_int64),
+        ("capacity_factor", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: "
+                         f"{lib().moe_status_str(status).decode()}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m sparse_mixture_experts_24_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        D = ctypes.POINTER(MoeDesc)
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [I]
+        L.moe_validate.restype = I
+        L.moe_validate.argtypes = [D]
+        L.moe_workspace_bytes.restype = S
+        L.moe_workspace_bytes.argtypes = [D]
+        L.moe_capacity.restype = ctypes.c_int64
+        L.moe_capacity.argtypes = [D]
+        L.moe_forward.restype = I
+        L.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_route.restype = I
+        L.moe_route.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
+        L.moe_dispatch.restype = I
+        L.moe_dispatch.argtypes = [D, P, P, P, P, P, P, S, P]
+        L.moe_experts.restype = I
+        L.moe_experts.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_experts_gate_up.restype = I
+        L.moe_experts_gate_up.argtypes = [D, P, P, P, P, P, P, P]
+        L.moe_experts_down.restype = I
+        L.moe_experts_down.argtypes = [D, P, P, P, P, P]
+        L.moe_combine.restype = I
+        L.moe_combine.argtypes = [D, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MOE_DTYPE_F32
+    if t == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def make_desc(T, d_model, n_experts, d_ff, top_k, n_shared=0, capacity_factor=0.0,
+              dtype=torch.bfloat16, out_dtype=None) -> MoeDesc:
+    return MoeDesc(int(T), int(d_model), int(n_experts), int(d_ff), int(top_k), int(n_shared),
+                   float(capacity_factor), _dt(dtype), _dt(out_dtype or dtype))
+
+
+def desc_for(x, W_router, W_gate, k, capacity_factor=0.0, out_dtype=None) -> MoeDesc:
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = W_gate.shape
+    return make_desc(T, d, E, F, k, G - E, capacity_factor, x.dtype, out_dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _require(t, name, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def workspace_bytes(desc: MoeDesc) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(desc)))
+
+
+def capacity(desc: MoeDesc):
+    c = int(lib().moe_capacity(ctypes.byref(desc)))
+    return None if c < 0 else c
+
+
+def validate(desc: MoeDesc) -> int:
+    return int(lib().moe_validate(ctypes.byref(desc)))
+
+
+def alloc_workspace(desc: MoeDesc, device) -> torch.Tensor:
+    n = workspace_bytes(desc)
+    if n == 0:
+        _check("moe_workspace_bytes", validate(desc) or 2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ws(desc, device, workspace):
+    if workspace is None:
+        workspace = alloc_workspace(desc, device)
+    return workspace
+
+
+def forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor=0.0,
+            out=None, f=None, p=None, out_dtype=None, workspace=None, want_stats=True):
+    """The whole MoE layer on the GPU.  Returns (y, f, p)."""
+    dev = x.device
+    desc = desc_for(x, W_router, W_gate, k, capacity_factor, out_dtype)
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = W_gate.shape
+    for t, n, shp in ((x, "x", (T, d)), (W_router, "W_router", (E, d)),
+                      (W_gate, "W_gate", (G, F, d)), (W_up, "W_up", (G, F, d)),
+                      (W_down, "W_down", (G, d, F))):
+        _require(t, n, dev, x.dtype, shp)
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    odt = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty(T, d, dtype=odt, device=dev)
+    if want_stats:
+        f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+        p = torch.empty(E, dtype=torch.float32, device=dev) if p is None else p
+    _require(out, "out", dev, odt, (T, d))
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(router_bias),
+                           _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(out), _ptr(f), _ptr(p),
+                           _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_forward", st)
+    return out, f, p
+
+
+def route(x, W_router, router_bias, k, workspace=None, W_gate_shape=None, n_shared=0):
+    """Router + top-k + renorm + statistics.  Returns (topk_idx, topk_w, f, p)."""
+    dev = x.device
+    T, d = x.shape
+    E = W_router.shape[0]
+    desc = make_desc(T, d, E, 64, k, n_shared, 0.0, x.dtype)
+    _require(x, "x", dev)
+    _require(W_router, "W_router", dev, x.dtype, (E, d))
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    p = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(router_bias),
+                         _ptr(idx), _ptr(w), _ptr(f), _ptr(p), _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_route", st)
+    return idx, w, f, p
+
+
+def dispatch(topk_idx, n_experts, capacity_factor=0.0, workspace=None):
+    """Histogram, capacity, offsets and the stable permutation.
+    Returns (counts, offsets, perm_src, slot_pos)."""
+    dev = topk_idx.device
+    T, k = topk_idx.shape
+    desc = make_desc(T, 64, n_experts, 64, k, 0, capacity_factor, torch.bfloat16)
+    _require(topk_idx, "topk_idx", dev, torch.int32)
+    counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    perm_src = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    slot_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                            _ptr(perm_src), _ptr(slot_pos), _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_dispatch", st)
+    return counts, offsets, perm_src, slot_pos
+
+
+def experts(x, perm_src, offsets, W_gate, W_up, W_down, k, n_experts, want_h=False,
+            workspace=None, capacity_factor=0.0):
+    """Grouped SwiGLU experts.  Returns (Yp [T*k + S*T, d] float32, H or None)."""
+    dev = x.device
+    T, d = x.shape
+    G, F, _ = W_gate.shape
+    desc = make_desc(T, d, n_experts, F, k, G - n_experts, capacity_factor, x.dtype)
+    for t, n, shp in ((x, "x", (T, d)), (W_gate, "W_gate", (G, F, d)),
+                      (W_up, "W_up", (G, F, d)), (W_down, "W_down", (G, d, F))):
+        _require(t, n, dev, x.dtype, shp)
+    _require(perm_src, "perm_src", dev, torch.int32)
+    _require(offsets, "offsets", dev, torch.int32, (n_experts + 1,))
+    rows = T * k + (G - n_experts) * T
+    Yp = torch.zeros(rows, d, dtype=torch.float32, device=dev)
+    H = torch.zeros(rows, F, dtype=x.dtype, device=dev) if want_h else None
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_experts(ctypes.byref(desc), _ptr(x), _ptr(perm_src), _ptr(offsets),
+                           _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Yp), _ptr(H), _ptr(ws),
+                           ws.numel(), _stream(dev))
+    _check("moe_experts", st)
+    return Yp, H
+
+
+def experts_gate_up(x, perm_src, offsets, W_gate, W_up, k, n_experts, H=None):
+    """Gate/up grouped GEMM with the fused SiLU*mul epilogue.  Returns H."""
+    dev = x.device
+    T, d = x.shape
+    G, F, _ = W_gate.shape
+    desc = make_desc(T, d, n_experts, F, k, G - n_experts, 0.0, x.dtype)
+    rows = T * k + (G - n_experts) * T
+    if H is None:
+        H = torch.empty(rows, F, dtype=x.dtype, device=dev)
+    _require(H, "H", dev, x.dtype, (rows, F))
+    st = lib().moe_experts_gate_up(ctypes.byref(desc), _ptr(x), _ptr(perm_src), _ptr(offsets),
+                                   _ptr(W_gate), _ptr(W_up), _ptr(H), _stream(dev))
+    _check("moe_experts_gate_up", st)
+    return H
+
+
+def experts_down(H, offsets, W_down, T, k, n_experts, Yp=None):
+    """Down grouped GEMM.  Returns Yp (float32)."""
+    dev = H.device
+    G, d, F = W_down.shape
+    desc = make_desc(T, d, n_experts, F, k, G - n_experts, 0.0, H.dtype)
+    rows = T * k + (G - n_experts) * T
+    if Yp is None:
+        Yp = torch.empty(rows, d, dtype=torch.float32, device=dev)
+    _require(Yp, "Yp", dev, torch.float32, (rows, d))
+    st = lib().moe_experts_down(ctypes.byref(desc), _ptr(H), _ptr(offsets), _ptr(W_down),
+                                _ptr(Yp), _stream(dev))
+    _check("moe_experts_down", st)
+    return Yp
+
+
+def combine(Yp, slot_pos, topk_w, T, d, k, n_shared=0, out_dtype=torch.float32, n_experts=None):
+    """Weighted combine back to token order.  Returns out [T, d]."""
+    dev = Yp.device
+    E = n_experts or k
+    desc = make_desc(T, d, E, 64, k, n_shared, 0.0, torch.bfloat16, out_dtype)
+    _require(Yp, "Yp", dev, torch.float32)
+    _require(slot_pos, "slot_pos", dev, torch.int32)
+    _require(topk_w, "topk_w", dev, torch.float32)
+    out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    st = lib().moe_combine(ctypes.byref(desc), _ptr(Yp), _ptr(slot_pos), _ptr(topk_w), _ptr(out),
+                           _stream(dev))
+    _check("moe_combine", st)
+    return out
+
+
+class MoELayer:
+    """Holds the layer's device weights and a reusable workspace."""
+
+    def __init__(self, W_router, W_gate, W_up, W_down, k, capacity_factor=0.0,
+                 router_bias=None, out_dtype=None):
+        self.W_router, self.W_gate, self.W_up, self.W_down = W_router, W_gate, W_up, W_down
+        self.router_bias = router_bias
+        self.k = int(k)
+        self.capacity_factor = float(capacity_factor)
+        self.out_dtype = out_dtype
+        self._ws = None
+        self._ws_T = None
+
+    def __call__(self, x, out=None, f=None, p=None):
+        if self._ws is None or self._ws_T != x.shape[0]:
+            desc = desc_for(x, self.W_router, self.W_gate, self.k, self.capacity_factor,
+                            self.out_dtype)
+            self._ws = alloc_workspace(desc, x.device)
+            self._ws_T = x.shape[0]
+        return forward(x, self.W_router, self.router_bias, self.W_gate, self.W_up, self.W_down,
+                       self.k, self.capacity_factor, out=out, f=f, p=p, out_dtype=self.out_dtype,
+                       workspace=self._ws)

@@ -1,0 +1,405 @@
+// Grouped SwiGLU experts: for every expert (group) g the rows [row_begin_g,
+// row_begin_g + M_g) of the expert-contiguous order run through
+//   H = SiLU(X W_gate[g]^T) * (X W_up[g]^T)      (gate/up GEMM, fused epilogue)
+//   Yp = H W_down[g]^T                             (down GEMM)
+// "Chapter 30: Mixture of Experts" (LLM Transformer book), 30.2.4: w1 through SiLU,
+// w3 linear, w2 back to d; "Mixture-of-experts in practice" (deepseekmodel.com),
+// expert-parallel section: with the tokens of each expert contiguous, one grouped GEMM
+// computes all experts of the layer at once instead of one small GEMM per expert.
+//
+// bf16 kernel (gfx950):
+//   * one 256x256 output tile per iteration of a persistent loop; 4 wave64s, each a
+//     128x128 sub-tile held in 16 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per
+//     lane); for the gate/up GEMM a wave's 128 columns are 64 gate + the matching 64 up
+//     columns, so SiLU(g)*u is formed in registers and H is stored once, in bf16;
+//   * K is walked in 64-wide steps through two LDS stages (rows padded to 72 bf16 so
+//     that a wavefront's 16-byte fragment reads hit distinct banks); the next step's
+//     global loads are in flight while the current step's 64 MFMAs run;
+//   * the X rows of the gate/up GEMM are gathered on the fly through perm_src (the
+//     permuted activations are never materialised);
+//   * the tile table (per-group m-tile prefix) is built on the device from the
+//     dispatch offsets, so skewed per-expert counts need no host round trip; tiles are
+//     ordered (group, n-tile, m-tile), and each XCD takes a contiguous run of them, so
+//     the m-tiles that share a weight tile run on the same L2.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+  const void* A;          // gated: x [T, K]; down: H [rows, K]
+  const int32_t* perm_src;
+  const int32_t* offsets; // [E+1]
+  const void* B0;         // gated: W_gate; down: W_down   [G, N, K]
+  const void* B1;         // gated: W_up
+  void* out;              // gated: H [rows, N] (dtype); down: Yp [rows, N] fp32
+  int64_t shared_row0;    // T*k: first row of the shared expert
+  int T, topk, E, G, N, K, n_tiles;
+};
+
+// Geometry of group g.
+__device__ inline void group_rows(const GemmArgs& a, int g, int64_t& row_begin, int& M) {
+  if (g < a.E) {
+    row_begin = a.offsets[g];
+    M = a.offsets[g + 1] - a.offsets[g];
+  } else {
+    row_begin = a.shared_row0;
+    M = a.T;
+  }
+}
+
+// Builds, in LDS, the exclusive prefix over groups of ceil(M_g / bm) (the m-tile
+// table) from the dispatch offsets; tiles[G] is the total.  Wavefront 0 scans the
+// groups 64 at a time.  Ends with a barrier.
+__device__ inline void build_tile_table(const GemmArgs& a, int bm, int* tiles) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int run = 0;
+    for (int base = 0; base < a.G; base += 64) {
+      const int g = base + lane;
+      int c = 0;
+      if (g < a.G) {
+        const int M = (g < a.E) ? a.offsets[g + 1] - a.offsets[g] : a.T;
+        c = (M + bm - 1) / bm;
+      }
+      int incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (g < a.G) tiles[g] = run + incl - c;
+      run += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) tiles[a.G] = run;
+  }
+  __syncthreads();
+}
+
+// tile -> group; tiles are ordered (group, n-tile, m-tile).
+__device__ inline int find_group(const int* tiles, int G, int n_tiles, int64_t tile) {
+  int lo = 0, hi = G;     // tiles[lo]*n_tiles <= tile < tiles[hi]*n_tiles
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)tiles[mid] * n_tiles <= tile) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Source row (in A) of row m of group g, for m < M.
+template <bool GATED>
+__device__ inline int64_t a_source_row(const GemmArgs& a, int g, int64_t row_begin, int m) {
+  if (!GATED) return row_begin + m;                 // H rows are already grouped
+  if (g < a.E) return a.perm_src[row_begin + m] / a.topk;
+  return m;                                          // shared expert: token m
+}
+
+__device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8;
+constexpr int STAGE = (BM + BN) * LDK;                       // bf16 elements per stage
+constexpr size_t GEMM_LDS_BYTES = 2 * STAGE * sizeof(bf16_t);  // 147456
+
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;   // load row (0..31) and k offset
+  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row and k offset
+  const bf16_t* A = (const bf16_t*)a.A;
+  const bf16_t* B0 = (const bf16_t*)a.B0;
+  const bf16_t* B1 = (const bf16_t*)a.B1;
+  const int K = a.K, N = a.N;
+  const int nk = K / BK;
+  __shared__ int tiles[kMaxExperts + 2];
+  build_tile_table(a, BM, tiles);
+  const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
+  const int per = gridDim.x >> 3;
+  const int64_t first = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+
+  for (int64_t tile = first; tile < total; tile += gridDim.x) {
+    const int g = find_group(tiles, a.G, a.n_tiles, tile);
+    int64_t row_begin;
+    int M;
+    group_rows(a, g, row_begin, M);
+    const int mt_g = tiles[g + 1] - tiles[g];
+    const int64_t local = tile - (int64_t)tiles[g] * a.n_tiles;
+    const int m0 = (int)(local % mt_g) * BM;
+    const int ncol0 = (int)(local / mt_g) * (GATED ? BN / 2 : BN);
+
+    // Element offsets (32-bit: the host bounds T*d, rows*F and F*d below 2^31) of the 8
+    // A rows and 8 B rows this thread loads.
+    int aoff[8], boff[8];
+    const bf16_t* Bg = B0 + (int64_t)g * N * K;
+    const bf16_t* Bu = GATED ? B1 + (int64_t)g * N * K : Bg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + lr + 32 * i;
+      aoff[i] = (int)a_source_row<GATED>(a, g, row_begin, m < M ? m : 0) * K + lc;
+      // gated: rows [0,128) of the B tile are gate rows (i < 4), [128,256) up rows
+      const int nl = GATED ? ((lr + 32 * i) & 127) : (lr + 32 * i);
+      boff[i] = min(ncol0 + nl, N - 1) * K + lc;
+    }
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint4 ra[8], rb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = *reinterpret_cast<const uint4*>(A + aoff[i]);
+      rb[i] = *reinterpret_cast<const uint4*>((i < 4 ? Bg : Bu) + boff[i]);
+    }
+    {
+      bf16_t* As = smem;
+      bf16_t* Bs = smem + BM * LDK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint4*>(As + (lr + 32 * i) * LDK + lc) = ra[i];
+        *reinterpret_cast<uint4*>(Bs + (lr + 32 * i) * LDK + lc) = rb[i];
+      }
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const int koff = (kt + 1) * BK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ra[i] = *reinterpret_cast<const uint4*>(A + aoff[i] + koff);
+          rb[i] = *reinterpret_cast<const uint4*>((i < 4 ? Bg : Bu) + boff[i] + koff);
+        }
+      }
+      const bf16_t* As = smem + (kt & 1) * STAGE;
+      const bf16_t* Bs = As + BM * LDK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          af[mb] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + mb * 32 + fr) * LDK + ks * 16 + fk);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          int brow;
+          if (GATED) brow = (nb < 2) ? (wn * 64 + nb * 32 + fr) : (128 + wn * 64 + (nb - 2) * 32 + fr);
+          else brow = wn * 128 + nb * 32 + fr;
+          bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + brow * LDK + ks * 16 + fk);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      }
+      if (more) {
+        bf16_t* As2 = smem + ((kt + 1) & 1) * STAGE;
+        bf16_t* Bs2 = As2 + BM * LDK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          *reinterpret_cast<uint4*>(As2 + (lr + 32 * i) * LDK + lc) = ra[i];
+          *reinterpret_cast<uint4*>(Bs2 + (lr + 32 * i) * LDK + lc) = rb[i];
+        }
+      }
+      __syncthreads();
+    }
+
+    // Epilogue.  D[m][n] of a 32x32 block: lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
+    if (GATED) {
+      bf16_t* H = (bf16_t*)a.out;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = ncol0 + wn * 64 + nb * 32 + fr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < M && n < N) {
+              const float h = silu_f(acc[mb][nb][r]) * acc[mb][nb + 2][r];
+              H[(row_begin + m) * N + n] = f32_to_bf16(h);
+            }
+          }
+        }
+    } else {
+      float* Y = (float*)a.out;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = ncol0 + wn * 128 + nb * 32 + fr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
+          }
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 kernel
+// Plain FMA tiles of 64x64 (gate/up: 64 rows x 64 gate + 64 up columns), BK 16.
+template <bool GATED>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  constexpr int TM = 64, TN = 64, TK = 16;
+  __shared__ float As[TK][TM + 4];
+  __shared__ float Bs[GATED ? 2 : 1][TK][TN + 4];
+  __shared__ int tiles[kMaxExperts + 2];
+  build_tile_table(a, TM, tiles);
+  const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
+  const int64_t tile = blockIdx.x;
+  if (tile >= total) return;
+  const int g = find_group(tiles, a.G, a.n_tiles, tile);
+  int64_t row_begin;
+  int M;
+  group_rows(a, g, row_begin, M);
+  const int mt_g = tiles[g + 1] - tiles[g];
+  const int64_t local = tile - (int64_t)tiles[g] * a.n_tiles;
+  const int m0 = (int)(local % mt_g) * TM;
+  const int n0 = (int)(local / mt_g) * TN;
+  const float* A = (const float*)a.A;
+  const float* B0 = (const float*)a.B0;
+  const float* B1 = (const float*)a.B1;
+  const int K = a.K, N = a.N;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[2][4][4] = {};
+  // loader: 64 rows x 16 k = 1024 floats = 256 threads x 4
+  const int lrow = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;
+  const int am = m0 + lrow;
+  const int64_t asrc = a_source_row<GATED>(a, g, row_begin, am < M ? am : 0);
+  const int bn = min(n0 + lrow, N - 1);
+  for (int k0 = 0; k0 < K; k0 += TK) {
+    const float4 va = *reinterpret_cast<const float4*>(A + asrc * K + k0 + lk);
+    As[lk + 0][lrow] = va.x; As[lk + 1][lrow] = va.y; As[lk + 2][lrow] = va.z; As[lk + 3][lrow] = va.w;
+    const float4 vb = *reinterpret_cast<const float4*>(B0 + ((int64_t)g * N + bn) * K + k0 + lk);
+    Bs[0][lk + 0][lrow] = vb.x; Bs[0][lk + 1][lrow] = vb.y; Bs[0][lk + 2][lrow] = vb.z; Bs[0][lk + 3][lrow] = vb.w;
+    if (GATED) {
+      const float4 vu = *reinterpret_cast<const float4*>(B1 + ((int64_t)g * N + bn) * K + k0 + lk);
+      Bs[GATED ? 1 : 0][lk + 0][lrow] = vu.x; Bs[GATED ? 1 : 0][lk + 1][lrow] = vu.y;
+      Bs[GATED ? 1 : 0][lk + 2][lrow] = vu.z; Bs[GATED ? 1 : 0][lk + 3][lrow] = vu.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float av[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int q = 0; q < (GATED ? 2 : 1); ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float bv = Bs[q][kk][tx * 4 + j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[q][i][j] = fmaf(av[i], bv, acc[q][i][j]);
+        }
+    }
+    __syncthreads();
+  }
+  float* out = (float*)a.out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const float v = GATED ? silu_f(acc[0][i][j]) * acc[1][i][j] : acc[0][i][j];
+      out[(row_begin + m) * N + n] = v;
+    }
+  }
+}
+
+static int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <bool GATED>
+static hipError_t run_bf16(const GemmArgs& a, int64_t max_m_tiles, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)GEMM_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t upper = max_m_tiles * a.n_tiles;
+  int64_t grid = device_cu_count();
+  if (upper < grid) grid = upper;
+  grid = round_up(grid, 8);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_bf16_kernel<GATED>, dim3((unsigned)grid), dim3(256), GEMM_LDS_BYTES, s, a);
+  return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t run_f32(const GemmArgs& a, int64_t max_m_tiles, hipStream_t s) {
+  const int64_t grid = max_m_tiles * a.n_tiles;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel<GATED>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+static GemmArgs base_args(const moe_desc_t& d, const int32_t* offsets) {
+  GemmArgs a{};
+  a.offsets = offsets;
+  a.shared_row0 = d.T * d.top_k;
+  a.T = (int)d.T;
+  a.topk = (int)d.top_k;
+  a.E = (int)d.n_experts;
+  a.G = (int)(d.n_experts + d.n_shared);
+  return a;
+}
+
+// Upper bound of sum_g ceil(M_g / bm): ceil(T*k / bm) + E (+ ceil(T / bm) shared).
+static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
+  return ceil_div(d.T * d.top_k, bm) + d.n_experts + (d.n_shared ? ceil_div(d.T, bm) : 0);
+}
+
+hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
+                          const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
+                          hipStream_t s) {
+  const bool bf = d.dtype == MOE_DTYPE_BF16;
+  GemmArgs a = base_args(d, offsets);
+  a.A = x;
+  a.perm_src = perm_src;
+  a.B0 = W_gate;
+  a.B1 = W_up;
+  a.out = H;
+  a.N = (int)d.d_ff;
+  a.K = (int)d.d_model;
+  a.n_tiles = (int)ceil_div(d.d_ff, bf ? BN / 2 : 64);
+  return bf ? run_bf16<true>(a, max_m_tiles(d, BM), s) : run_f32<true>(a, max_m_tiles(d, 64), s);
+}
+
+hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
+                       const void* W_down, float* Yp, hipStream_t s) {
+  const bool bf = d.dtype == MOE_DTYPE_BF16;
+  GemmArgs a = base_args(d, offsets);
+  a.A = H;
+  a.B0 = W_down;
+  a.out = Yp;
+  a.N = (int)d.d_model;
+  a.K = (int)d.d_ff;
+  a.n_tiles = (int)ceil_div(d.d_model, bf ? BN : 64);
+  return bf ? run_bf16<false>(a, max_m_tiles(d, BM), s) : run_f32<false>(a, max_m_tiles(d, 64), s);
+}
+
+}  // namespace moe

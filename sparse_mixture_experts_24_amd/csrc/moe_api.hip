@@ -1,0 +1,233 @@
+// C ABI of libmoe: argument validation, workspace carving and the launch sequence of
+// the layer's forward pass.  The contract of every entry point is documented in
+// include/moe.h.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static moe_status_t validate(const moe_desc_t* d) {
+  if (!d) return MOE_E_NULL;
+  if (d->T < 0 || d->d_model <= 0 || d->n_experts < 1 || d->d_ff <= 0 || d->top_k < 1 ||
+      d->top_k > d->n_experts || d->n_shared < 0 || d->n_shared > 1 ||
+      !isfinite(d->capacity_factor))
+    return MOE_E_SHAPE;
+  if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16) return MOE_E_UNSUPPORTED;
+  if (d->out_dtype != MOE_DTYPE_F32 && d->out_dtype != MOE_DTYPE_BF16) return MOE_E_UNSUPPORTED;
+  if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_E_UNSUPPORTED;
+  if (d->d_model % 64 || d->d_ff % 64 || d->d_model > 65536 || d->d_ff > 65536)
+    return MOE_E_UNSUPPORTED;
+  const int64_t rows = d->T * d->top_k + d->n_shared * d->T;
+  // 32-bit element offsets inside the kernels
+  if (d->T > (int64_t)INT32_MAX / 32 || rows > (int64_t)INT32_MAX ||
+      d->T * d->d_model > (int64_t)INT32_MAX || rows * d->d_ff > (int64_t)INT32_MAX ||
+      d->d_ff * d->d_model > (int64_t)INT32_MAX)
+    return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace carve_workspace(const moe_desc_t& d, void* base) {
+  const RoutePlan rp = route_plan(d);
+  const int64_t TK = d.T * d.top_k, E = d.n_experts;
+  const int64_t rows = TK + d.n_shared * d.T;
+  const int64_t nbd = ceil_div(TK, kDispatchChunk);
+  const int64_t nbh = rp.n_blocks > nbd ? rp.n_blocks : nbd;
+  const size_t esz = d.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  char* p = (char*)base;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? (void*)(p + off) : nullptr;
+    off += align256(bytes > 0 ? bytes : 1);
+    return r;
+  };
+  Workspace w{};
+  w.topk_idx = (int32_t*)take(TK * 4);
+  w.topk_w = (float*)take(TK * 4);
+  w.p_part = (float*)take(rp.n_blocks * E * 4);
+  w.cnt_part = (int32_t*)take(nbh * E * 4);
+  w.counts = (int32_t*)take(E * 4);
+  w.offsets = (int32_t*)take((E + 1) * 4);
+  w.perm_src = (int32_t*)take(TK * 4);
+  w.slot_pos = (int32_t*)take(TK * 4);
+  w.H = take((size_t)rows * d.d_ff * esz);
+  w.Yp = (float*)take((size_t)rows * d.d_model * 4);
+  w.bytes = off;
+  return w;
+}
+
+static moe_status_t check_ws(const moe_desc_t& d, void* ws, size_t bytes, Workspace& w) {
+  w = carve_workspace(d, ws);
+  if (!ws || bytes < w.bytes || ((uintptr_t)ws & 255u)) return MOE_E_WORKSPACE;
+  return MOE_OK;
+}
+
+static int64_t capacity_of(const moe_desc_t& d) {
+  if (!(d.capacity_factor > 0.0f)) return -1;
+  const double c = floor((double)d.capacity_factor * (double)d.top_k * (double)d.T /
+                         (double)d.n_experts);
+  int64_t C = (int64_t)c;
+  if (C < d.top_k) C = d.top_k;
+  return C;
+}
+
+#define MOE_HIP(call)                       \
+  do {                                      \
+    if ((call) != hipSuccess) return MOE_E_HIP; \
+  } while (0)
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_NULL: return "MOE_E_NULL: a required pointer is NULL";
+    case MOE_E_SHAPE: return "MOE_E_SHAPE: inconsistent or out-of-range sizes";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: outside what the kernels implement";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_E_HIP: return "MOE_E_HIP: a HIP launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_validate(const moe_desc_t* desc) { return validate(desc); }
+
+size_t moe_workspace_bytes(const moe_desc_t* desc) {
+  if (validate(desc) != MOE_OK) return 0;
+  return carve_workspace(*desc, nullptr).bytes;
+}
+
+int64_t moe_capacity(const moe_desc_t* desc) {
+  if (validate(desc) != MOE_OK) return -1;
+  return capacity_of(*desc);
+}
+
+moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_router,
+                       const float* router_bias, int32_t* topk_idx, float* topk_w, float* f,
+                       float* p, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!x || !W_router || !topk_idx || !topk_w) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_router)) return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, w.p_part, w.cnt_part, s));
+  MOE_HIP(launch_stats(d, w.p_part, w.cnt_part, rp.n_blocks, f, p, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_src, int32_t* slot_pos,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!topk_idx || !counts || !offsets || !perm_src || !slot_pos) return MOE_E_NULL;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t TK = d.T * d.top_k;
+  const int E = (int)d.n_experts;
+  const int64_t C = capacity_of(d);
+  MOE_HIP(launch_hist(topk_idx, TK, E, kDispatchChunk, w.cnt_part, s));
+  MOE_HIP(launch_scan(w.cnt_part, ceil_div(TK, kDispatchChunk), E, C, counts, offsets, s));
+  MOE_HIP(launch_scatter(topk_idx, TK, E, kDispatchChunk, C, w.cnt_part, offsets, perm_src,
+                         slot_pos, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                         const int32_t* offsets, const void* W_gate, const void* W_up,
+                         const void* W_down, float* Yp, void* H, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!x || !perm_src || !offsets || !W_gate || !W_up || !W_down || !Yp) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+      !aligned16(Yp) || (H && !aligned16(H)))
+    return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  void* h = H ? H : w.H;
+  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, W_gate, W_up, h, s));
+  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_experts_gate_up(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                                 const int32_t* offsets, const void* W_gate, const void* W_up,
+                                 void* H, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (!x || !perm_src || !offsets || !W_gate || !W_up || !H) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(H))
+    return MOE_E_UNSUPPORTED;
+  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, W_gate, W_up, H, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32_t* offsets,
+                              const void* W_down, float* Yp, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (!H || !offsets || !W_down || !Yp) return MOE_E_NULL;
+  if (!aligned16(H) || !aligned16(W_down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
+  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t* slot_pos,
+                         const float* topk_w, void* out, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!Yp || !slot_pos || !topk_w || !out) return MOE_E_NULL;
+  if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
+  MOE_HIP(launch_combine(d, Yp, slot_pos, topk_w, out, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_router,
+                         const float* router_bias, const void* W_gate, const void* W_up,
+                         const void* W_down, void* out, float* f, float* p, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !out) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_router) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down) || !aligned16(out))
+    return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  const int64_t TK = d.T * d.top_k;
+  const int E = (int)d.n_experts;
+  const int64_t C = capacity_of(d);
+  const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
+  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, w.p_part, w.cnt_part, s));
+  MOE_HIP(launch_stats(d, w.p_part, w.cnt_part, rp.n_blocks, f, p, s));
+  MOE_HIP(launch_scan(w.cnt_part, rp.n_blocks, E, C, w.counts, w.offsets, s));
+  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.offsets, w.perm_src,
+                         w.slot_pos, s));
+  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, s));
+  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, s));
+  MOE_HIP(launch_combine(d, w.Yp, w.slot_pos, w.topk_w, out, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

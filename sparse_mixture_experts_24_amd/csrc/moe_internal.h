@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libmoe (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+
+// Upper limits enforced by moe_validate.
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+__device__ inline float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- route plan
+// One route block handles BT = 16 * TPW tokens with 4 waves: EW waves split the
+// (padded) experts into slabs of 16 * EPW, KS = 4 / EW waves split the reduction.
+struct RoutePlan {
+  int EPW, TPW, KS, BT, E_pad;
+  int64_t n_blocks;
+};
+RoutePlan route_plan(const moe_desc_t& d);
+
+// ---------------------------------------------------------------- workspace
+struct Workspace {
+  int32_t* topk_idx;   // [T*k]
+  float* topk_w;       // [T*k]
+  float* p_part;       // [route blocks][E]
+  int32_t* cnt_part;   // [max(route blocks, dispatch blocks)][E]  (block histograms -> bases)
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]
+  int32_t* perm_src;   // [T*k]
+  int32_t* slot_pos;   // [T*k]
+  void* H;             // [T*k + S*T, F] dtype
+  float* Yp;           // [T*k + S*T, d]
+  size_t bytes;
+};
+Workspace carve_workspace(const moe_desc_t& d, void* base);
+
+constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe_dispatch
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* p_part,
+                        int32_t* cnt_part, hipStream_t s);
+hipError_t launch_stats(const moe_desc_t& d, const float* p_part, const int32_t* cnt_part,
+                        int64_t n_blocks, float* f, float* p, hipStream_t s);
+hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
+                       hipStream_t s);
+hipError_t launch_scan(int32_t* blk_cnt, int64_t n_blocks, int E, int64_t C, int32_t* counts,
+                       int32_t* offsets, hipStream_t s);
+hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int64_t C,
+                          const int32_t* blk_base, const int32_t* offsets, int32_t* perm_src,
+                          int32_t* slot_pos, hipStream_t s);
+hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
+                          const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
+                          hipStream_t s);
+hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
+                       const void* W_down, float* Yp, hipStream_t s);
+hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
+                          const float* topk_w, void* out, hipStream_t s);
+
+}  // namespace moe

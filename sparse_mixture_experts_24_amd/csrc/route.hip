@@ -1,0 +1,373 @@
+// Router: logits = x W_r^T, softmax, top-k on the selection score p + bias, renormalised
+// weights, per-block partial sums of p and per-block expert histograms.
+//
+// "Chapter 30: Mixture of Experts" (LLM Transformer book), 30.2.3 steps 1-4;
+// "Mixture of Experts (MoE) memo" (iwashi.co), DeepSeek-V3 aux-loss-free section (the
+// bias only changes the choice); "Mixture-of-experts in practice" (deepseekmodel.com),
+// routing-math section (bias-free gate, always renormalise).
+//
+// bf16 layers: the logits GEMM runs on MFMA (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation).  One block = 4 wave64s over BT tokens.  EW waves split the experts
+// into slabs of 16*EPW; KS = 4/EW waves split the reduction over d.  Each lane reads
+// 32 contiguous bytes of a row per 64-wide k chunk (a row's 128 bytes come from 4
+// lanes), and the two MFMAs of the chunk take the first and second 16 bytes: A and B
+// use the same k mapping, so the sum is over the same pairs as a plain dot product.
+// The top-k runs one wavefront per token with shuffle reductions.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Softmax + top-k + renorm for the tokens of one block, logits in LDS rows of E_PAD.
+// Waves take tokens tt = wave, wave + 4, ...  Accumulates p into psum (per lane, expert
+// lane + 64 i) and the chosen experts into the LDS histogram cnt.
+template <int E_PAD>
+__device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E, int k,
+                                  const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+                                  float* __restrict__ topk_w, float* psum, int* cnt) {
+  constexpr int NV = (E_PAD + 63) / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    bv[i] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+  }
+  for (int tt = w; tt < BT; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    const float* row = lg + (size_t)tt * E_PAD;
+    float v[NV];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (e < E) ? row[e] : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
+    m = wave_max(m);
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (e < E) ? expf(v[i] - m) : 0.0f;
+      sum += v[i];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.0f / sum;
+    float s[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = v[i] * inv;                       // p
+      psum[i] += v[i];
+      s[i] = (e < E) ? v[i] + bv[i] : -INFINITY;   // selection score, fp32
+    }
+    unsigned taken = 0;
+    int my_idx = 0;
+    float my_p = 0.0f;
+    for (int r = 0; r < k; ++r) {
+      float bvv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        if (!((taken >> i) & 1u) && e < E && (s[i] > bvv || (s[i] == bvv && e < be))) {
+          bvv = s[i];
+          be = e;
+        }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bvv, o, 64);
+        const int oe = __shfl_xor(be, o, 64);
+        if (ov > bvv || (ov == bvv && oe < be)) {
+          bvv = ov;
+          be = oe;
+        }
+      }
+      const bool ok = be < E;   // always true for finite inputs and k <= E
+      const int owner = ok ? (be & 63) : 0, slot = ok ? (be >> 6) : 0;
+      float pp = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (i == slot) pp = v[i];
+      if (ok && lane == owner) taken |= 1u << slot;
+      pp = __shfl(pp, owner, 64);
+      if (lane == r) {
+        my_idx = be;
+        my_p = pp;
+      }
+      if (lane == 0 && be < E) atomicAdd(&cnt[be], 1);
+    }
+    float tot = 0.0f;
+    for (int r = 0; r < k; ++r) tot += __shfl(my_p, r, 64);
+    if (lane < k) {
+      topk_idx[(size_t)t * k + lane] = my_idx;
+      topk_w[(size_t)t * k + lane] = my_p / tot;
+    }
+  }
+}
+
+// Writes the block's partial sum of p and its expert histogram (fixed order).
+template <int E_PAD>
+__device__ inline void route_block_stats(const float* psum, float (*pw)[E_PAD], const int* cnt,
+                                         int E, float* __restrict__ p_part,
+                                         int32_t* __restrict__ cnt_part) {
+  constexpr int NV = (E_PAD + 63) / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < E_PAD) pw[w][lane + 64 * i] = psum[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    p_part[(size_t)blockIdx.x * E + e] = ((pw[0][e] + pw[1][e]) + pw[2][e]) + pw[3][e];
+    cnt_part[(size_t)blockIdx.x * E + e] = cnt[e];
+  }
+}
+
+template <int EPW, int TPW, int KS>
+__global__ __launch_bounds__(256) void route_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+  constexpr int EW = 4 / KS;
+  constexpr int E_PAD = 16 * EPW * EW;
+  constexpr int BT = 16 * TPW;
+  constexpr int NV = (E_PAD + 63) / 64;
+  __shared__ float lg[KS][BT][E_PAD];
+  __shared__ float pw[4][E_PAD];
+  __shared__ int cnt[E_PAD];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ew = w / KS, ks = w % KS;
+  const int t0 = blockIdx.x * BT;
+  const int r = lane & 15, g = lane >> 4;
+  for (int e = threadIdx.x; e < E_PAD; e += blockDim.x) cnt[e] = 0;
+
+  const bf16_t* arow[TPW];
+#pragma unroll
+  for (int tb = 0; tb < TPW; ++tb) {
+    const int t = min(t0 + tb * 16 + r, T - 1);
+    arow[tb] = x + (size_t)t * d + g * 16;
+  }
+  const bf16_t* brow[EPW];
+  bool bok[EPW];
+#pragma unroll
+  for (int eb = 0; eb < EPW; ++eb) {
+    const int e = (ew * EPW + eb) * 16 + r;
+    bok[eb] = e < E;
+    brow[eb] = Wr + (size_t)min(e, E - 1) * d + g * 16;
+  }
+  floatx4 acc[TPW][EPW];
+#pragma unroll
+  for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+    for (int eb = 0; eb < EPW; ++eb) acc[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = d / 64;
+  for (int c = ks; c < nchunk; c += KS) {
+    bf16x8 a0[TPW], a1[TPW], b0[EPW], b1[EPW];
+#pragma unroll
+    for (int tb = 0; tb < TPW; ++tb) {
+      const bf16x8* pa = reinterpret_cast<const bf16x8*>(arow[tb] + c * 64);
+      a0[tb] = pa[0];
+      a1[tb] = pa[1];
+    }
+#pragma unroll
+    for (int eb = 0; eb < EPW; ++eb) {
+      const bf16x8* pb = reinterpret_cast<const bf16x8*>(brow[eb] + c * 64);
+      b0[eb] = pb[0];
+      b1[eb] = pb[1];
+      if (!bok[eb]) {
+        b0[eb] = bf16x8{};
+        b1[eb] = bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+      for (int eb = 0; eb < EPW; ++eb) {
+        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[tb], b0[eb], acc[tb][eb], 0, 0, 0);
+        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[tb], b1[eb], acc[tb][eb], 0, 0, 0);
+      }
+  }
+  // D[m][n] of a 16x16 MFMA block sits in lane n + 16*(m/4), register m%4.
+#pragma unroll
+  for (int tb = 0; tb < TPW; ++tb)
+#pragma unroll
+    for (int eb = 0; eb < EPW; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lg[ks][tb * 16 + 4 * g + i][(ew * EPW + eb) * 16 + r] = acc[tb][eb][i];
+  __syncthreads();
+  if (KS > 1) {
+    for (int idx = threadIdx.x; idx < BT * E_PAD; idx += blockDim.x) {
+      float* base = &lg[0][0][0];
+      float v = base[idx];
+      for (int q = 1; q < KS; ++q) v += base[q * BT * E_PAD + idx];
+      base[idx] = v;
+    }
+    __syncthreads();
+  }
+  float psum[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
+  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, psum, cnt);
+  __syncthreads();
+  route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
+}
+
+// fp32 layers: plain FMA dot products (small correctness-sized layers).
+template <int E_PAD>
+__global__ __launch_bounds__(256) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+  constexpr int BT = 16;
+  constexpr int NV = (E_PAD + 63) / 64;
+  __shared__ float lg[BT][E_PAD];
+  __shared__ float pw[4][E_PAD];
+  __shared__ int cnt[E_PAD];
+  const int t0 = blockIdx.x * BT;
+  for (int e = threadIdx.x; e < E_PAD; e += blockDim.x) cnt[e] = 0;
+  for (int idx = threadIdx.x; idx < BT * E; idx += blockDim.x) {
+    const int tt = idx / E, e = idx % E;
+    const int t = min(t0 + tt, T - 1);
+    const float4* xa = reinterpret_cast<const float4*>(x + (size_t)t * d);
+    const float4* wb = reinterpret_cast<const float4*>(Wr + (size_t)e * d);
+    float acc = 0.0f;
+    for (int i = 0; i < d / 4; ++i) {
+      const float4 a = xa[i], b = wb[i];
+      acc = fmaf(a.x, b.x, acc);
+      acc = fmaf(a.y, b.y, acc);
+      acc = fmaf(a.z, b.z, acc);
+      acc = fmaf(a.w, b.w, acc);
+    }
+    lg[tt][e] = acc;
+  }
+  __syncthreads();
+  float psum[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
+  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, psum, cnt);
+  __syncthreads();
+  route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
+}
+
+RoutePlan route_plan(const moe_desc_t& d) {
+  RoutePlan p{};
+  const int E = (int)d.n_experts;
+  if (d.dtype == MOE_DTYPE_F32) {
+    int ep = 64;
+    while (ep < E) ep *= 2;
+    p.EPW = 0;
+    p.TPW = 1;
+    p.KS = 1;
+    p.BT = 16;
+    p.E_pad = ep;
+  } else {
+    int EW;
+    if (E <= 16) {
+      EW = 1;
+      p.EPW = 1;
+    } else if (E <= 32) {
+      EW = 2;
+      p.EPW = 1;
+    } else {
+      EW = 4;
+      int epw = 1;
+      while (epw * 64 < E) epw *= 2;
+      p.EPW = epw;
+    }
+    p.KS = 4 / EW;
+    p.TPW = (EW == 4 && p.EPW <= 4 && ceil_div(d.T, 32) >= 256) ? 2 : 1;
+    p.BT = 16 * p.TPW;
+    p.E_pad = 16 * p.EPW * EW;
+  }
+  p.n_blocks = ceil_div(d.T, p.BT);
+  return p;
+}
+
+hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* p_part,
+                        int32_t* cnt_part, hipStream_t s) {
+  const RoutePlan rp = route_plan(d);
+  if (rp.n_blocks == 0) return hipSuccess;
+  const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts, k = (int)d.top_k;
+  const dim3 grid((unsigned)rp.n_blocks), block(256);
+  if (d.dtype == MOE_DTYPE_F32) {
+    const float* xx = (const float*)x;
+    const float* ww = (const float*)W_router;
+#define MOE_ROUTE_F32(EP)                                                                     \
+  if (rp.E_pad == EP) {                                                                       \
+    hipLaunchKernelGGL(route_f32_kernel<EP>, grid, block, 0, s, xx, ww, bias, T, dm, E, k,    \
+                       topk_idx, topk_w, p_part, cnt_part);                                   \
+    return hipGetLastError();                                                                 \
+  }
+    MOE_ROUTE_F32(64)
+    MOE_ROUTE_F32(128)
+    MOE_ROUTE_F32(256)
+    MOE_ROUTE_F32(512)
+#undef MOE_ROUTE_F32
+    return hipErrorInvalidValue;
+  }
+  const bf16_t* xx = (const bf16_t*)x;
+  const bf16_t* ww = (const bf16_t*)W_router;
+#define MOE_ROUTE_BF16(EPW_, TPW_, KS_)                                                      \
+  if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
+    hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_>), grid, block, 0, s, xx, ww, bias, \
+                       T, dm, E, k, topk_idx, topk_w, p_part, cnt_part);                      \
+    return hipGetLastError();                                                                 \
+  }
+  MOE_ROUTE_BF16(1, 1, 4)
+  MOE_ROUTE_BF16(1, 1, 2)
+  MOE_ROUTE_BF16(1, 1, 1)
+  MOE_ROUTE_BF16(1, 2, 1)
+  MOE_ROUTE_BF16(2, 1, 1)
+  MOE_ROUTE_BF16(2, 2, 1)
+  MOE_ROUTE_BF16(4, 1, 1)
+  MOE_ROUTE_BF16(4, 2, 1)
+  MOE_ROUTE_BF16(8, 1, 1)
+#undef MOE_ROUTE_BF16
+  return hipErrorInvalidValue;
+}
+
+// f_e = sum_b cnt_part[b][e] / (T k);  P_e = sum_b p_part[b][e] / T   (fixed order)
+__global__ void stats_kernel(const float* __restrict__ p_part, const int32_t* __restrict__ cnt_part,
+                             int64_t n_blocks, int E, int64_t T, int k, float* __restrict__ f,
+                             float* __restrict__ p) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  float ps = 0.0f;
+  int64_t c = 0;
+  for (int64_t b = 0; b < n_blocks; ++b) {
+    ps += p_part[b * E + e];
+    c += cnt_part[b * E + e];
+  }
+  if (f) f[e] = T > 0 ? (float)((double)c / (double)(T * k)) : 0.0f;
+  if (p) p[e] = T > 0 ? (float)((double)ps / (double)T) : 0.0f;
+}
+
+hipError_t launch_stats(const moe_desc_t& d, const float* p_part, const int32_t* cnt_part,
+                        int64_t n_blocks, float* f, float* p, hipStream_t s) {
+  if (!f && !p) return hipSuccess;
+  const int E = (int)d.n_experts;
+  hipLaunchKernelGGL(stats_kernel, dim3((unsigned)ceil_div(E, 256)), dim3(256), 0, s, p_part,
+                     cnt_part, n_blocks, E, d.T, (int)d.top_k, f, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

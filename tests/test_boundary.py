@@ -1,0 +1,134 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching the GPU.  No compute
+call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import sparse_mixture_experts_24_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_mixture_experts_24_amd import build
+        build.build()
+    return moe.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_combine",
+              "moe_workspace_bytes", "moe_status_str", "moe_validate", "moe_capacity"):
+        assert n in names
+    assert sorted(moe.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    for n in header_functions():
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def desc(**kw):
+    base = dict(T=100, d_model=256, n_experts=8, d_ff=512, top_k=2, n_shared=0,
+                capacity_factor=0.0, dtype=moe.MOE_DTYPE_BF16, out_dtype=moe.MOE_DTYPE_BF16)
+    base.update(kw)
+    return moe.MoeDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"T": 0}, 0),
+    ({"T": -1}, 2),
+    ({"top_k": 0}, 2),
+    ({"top_k": 9}, 2),
+    ({"n_experts": 0}, 2),
+    ({"n_shared": 2}, 2),
+    ({"capacity_factor": float("nan")}, 2),
+    ({"capacity_factor": float("inf")}, 2),
+    ({"d_model": 100}, 3),
+    ({"d_ff": 96}, 3),
+    ({"n_experts": 513, "top_k": 2}, 3),
+    ({"n_experts": 64, "top_k": 17}, 3),
+    ({"dtype": 7}, 3),
+    ({"out_dtype": 2}, 3),
+    ({"n_experts": 512, "top_k": 16, "n_shared": 1}, 0),
+])
+def test_validate(L, kw, status):
+    d = desc(**kw)
+    assert L.moe_validate(ctypes.byref(d)) == status
+    assert (L.moe_workspace_bytes(ctypes.byref(d)) > 0) == (status == 0)
+    assert L.moe_validate(None) == 1
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert L.moe_status_str(code).decode().startswith(moe.STATUS[code])
+
+
+def test_capacity_matches_the_closed_form(L):
+    for T, E, k, cf in [(16384, 64, 1, 1.25), (10, 4, 1, 1.25), (3, 64, 2, 1.0), (4096, 8, 2, 1.1),
+                        (100, 8, 2, 0.0), (100, 8, 2, -1.0)]:
+        d = desc(T=T, n_experts=E, top_k=k, capacity_factor=cf)
+        c = L.moe_capacity(ctypes.byref(d))
+        ref = oracle.capacity(T, k, E, cf)
+        assert c == (-1 if ref is None else ref)
+
+
+def test_workspace_grows_with_tokens(L):
+    a = L.moe_workspace_bytes(ctypes.byref(desc(T=100)))
+    b = L.moe_workspace_bytes(ctypes.byref(desc(T=1000)))
+    c = L.moe_workspace_bytes(ctypes.byref(desc(T=1000, n_shared=1)))
+    assert 0 < a < b < c
+    assert a % 256 == 0
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch(L):
+    """Every check below fails on the host, so no HIP call is made."""
+    d = desc()
+    ws_need = L.moe_workspace_bytes(ctypes.byref(d))
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    P = ctypes.c_void_p
+    # NULL descriptor / NULL tensors
+    assert L.moe_forward(None, fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_forward(ctypes.byref(d), None, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_route(ctypes.byref(d), fake, fake, None, None, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_dispatch(ctypes.byref(d), fake, fake, None, fake, fake, fake, ws_need, None) == 1
+    assert L.moe_experts(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_combine(ctypes.byref(d), fake, fake, None, fake, None) == 1
+    # bad shapes
+    bad = desc(top_k=0)
+    assert L.moe_forward(ctypes.byref(bad), fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 2
+    assert L.moe_combine(ctypes.byref(bad), fake, fake, fake, fake, None) == 2
+    # workspace missing, too small or misaligned
+    assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, None, ws_need, None) == 4
+    assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need - 1, None) == 4
+    assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, P(0x100010), ws_need, None) == 4
+    assert L.moe_dispatch(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 0, None) == 4
+    # misaligned tensors
+    odd = P(0x100004)
+    assert L.moe_forward(ctypes.byref(d), odd, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 3
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe.so")
+    with pytest.raises(ImportError):
+        moe.lib()
