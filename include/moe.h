@@ -34,6 +34,8 @@
  *   - The library never allocates, frees or synchronises.  Scratch memory comes from
  *     the caller's workspace (size from moe_workspace_bytes).  Calls that share a
  *     workspace must not overlap; calls with distinct workspaces may run concurrently.
+ *   - With T == 0 the token-sized buffers (x, out, topk_*, perm_src, slot_pos, H, Yp)
+ *     may be NULL; weights, offsets and counts are always required.
  *   - All arguments are validated on the host before anything is enqueued; an invalid
  *     call returns a nonzero status and enqueues nothing.  MOE_E_HIP reports a failed
  *     kernel launch (hipGetLastError).  Non-finite inputs are undefined behaviour.

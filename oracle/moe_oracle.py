@@ -188,21 +188,25 @@ def dispatch(idx: np.ndarray, E: int, C=None):
 
 
 # ----------------------------------------------------------------------------- experts
-def expert_ffn(x_rows, Wg, Wu, Wd, h_bf16: bool) -> np.ndarray:
+def expert_ffn(x_rows, Wg, Wu, Wd, h_bf16: bool, return_h: bool = False):
     """One SwiGLU expert on a block of rows: o = W2( SiLU(W1 x) * W3 x ).
 
     [book ch.30] 30.2.4 and 30.6.1: w1 (gate) goes through SiLU, w3 (up) is linear,
     w2 (down) projects back; no biases.  Here Wg = w1 [F,d], Wu = w3 [F,d],
     Wd = w2 [d,F].  h = fp32(SiLU(g) * u), rounded to bf16 when the layer's
-    activations are bf16; o = fp32(W2 h).
+    activations are bf16; o = fp32(W2 h).  With return_h, also returns the float64 g, u
+    and h before any rounding (the tests use them to bound where a bf16 rounding of h
+    may legitimately go either way).
     """
     xr = np.asarray(x_rows, F64)
     g = xr @ np.asarray(Wg, F64).T
     u = xr @ np.asarray(Wu, F64).T
-    h = (silu(g) * u).astype(F32)
+    h64 = silu(g) * u
+    h = h64.astype(F32)
     if h_bf16:
         h = bf16_round(h)
-    return (h.astype(F64) @ np.asarray(Wd, F64).T).astype(F32)
+    o = (h.astype(F64) @ np.asarray(Wd, F64).T).astype(F32)
+    return (o, {"g": g, "u": u, "h": h64}) if return_h else o
 
 
 def combine(T, d, w, slot_pos, Y, shared=None) -> np.ndarray:

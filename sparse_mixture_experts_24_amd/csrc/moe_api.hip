@@ -116,7 +116,8 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
-  if (!x || !W_router || !topk_idx || !topk_w) return MOE_E_NULL;
+  const bool any = d.T > 0;   // with no tokens, token-sized buffers may be NULL
+  if (!W_router || (any && (!x || !topk_idx || !topk_w))) return MOE_E_NULL;
   if (!aligned16(x) || !aligned16(W_router)) return MOE_E_UNSUPPORTED;
   Workspace w;
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
@@ -133,7 +134,8 @@ moe_status_t moe_dispatch(const moe_desc_t* desc, const int32_t* topk_idx, int32
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
-  if (!topk_idx || !counts || !offsets || !perm_src || !slot_pos) return MOE_E_NULL;
+  if (!counts || !offsets || (d.T > 0 && (!topk_idx || !perm_src || !slot_pos)))
+    return MOE_E_NULL;
   Workspace w;
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -154,7 +156,9 @@ moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* p
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
-  if (!x || !perm_src || !offsets || !W_gate || !W_up || !W_down || !Yp) return MOE_E_NULL;
+  const bool any = d.T > 0;
+  if (!offsets || !W_gate || !W_up || !W_down || (any && (!x || !perm_src || !Yp)))
+    return MOE_E_NULL;
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
       !aligned16(Yp) || (H && !aligned16(H)))
     return MOE_E_UNSUPPORTED;
@@ -172,7 +176,8 @@ moe_status_t moe_experts_gate_up(const moe_desc_t* desc, const void* x, const in
                                  void* H, void* stream) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
-  if (!x || !perm_src || !offsets || !W_gate || !W_up || !H) return MOE_E_NULL;
+  if (!offsets || !W_gate || !W_up || (desc->T > 0 && (!x || !perm_src || !H)))
+    return MOE_E_NULL;
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(H))
     return MOE_E_UNSUPPORTED;
   MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, W_gate, W_up, H, (hipStream_t)stream));
@@ -183,7 +188,7 @@ moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32
                               const void* W_down, float* Yp, void* stream) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
-  if (!H || !offsets || !W_down || !Yp) return MOE_E_NULL;
+  if (!offsets || !W_down || (desc->T > 0 && (!H || !Yp))) return MOE_E_NULL;
   if (!aligned16(H) || !aligned16(W_down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
   MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, (hipStream_t)stream));
   return MOE_OK;
@@ -194,7 +199,7 @@ moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t*
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
-  if (!Yp || !slot_pos || !topk_w || !out) return MOE_E_NULL;
+  if (d.T > 0 && (!Yp || !slot_pos || !topk_w || !out)) return MOE_E_NULL;
   if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
   MOE_HIP(launch_combine(d, Yp, slot_pos, topk_w, out, (hipStream_t)stream));
   return MOE_OK;
@@ -207,7 +212,7 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
-  if (!x || !W_router || !W_gate || !W_up || !W_down || !out) return MOE_E_NULL;
+  if (!W_router || !W_gate || !W_up || !W_down || (d.T > 0 && (!x || !out))) return MOE_E_NULL;
   if (!aligned16(x) || !aligned16(W_router) || !aligned16(W_gate) || !aligned16(W_up) ||
       !aligned16(W_down) || !aligned16(out))
     return MOE_E_UNSUPPORTED;

@@ -63,3 +63,59 @@ def check_routing(idx_gpu, w_gpu, ref):
 
 def to_dev(inputs, device):
     return {k: (None if v is None else v.to(device)) for k, v in inputs.items()}
+
+
+def bf16_ulp(v):
+    """Spacing of bfloat16 numbers at |v| (8 significant bits)."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def fp32_dot_error(x, W):
+    """Statistical bound on the fp32 accumulation error of the dot products x W^T over K
+    terms: the products of bf16 values are exact, each of the K additions rounds with
+    relative error <= 2^-24 of a partial sum whose size grows like sqrt(i) times the rms
+    term, so the error has standard deviation ~ 2^-24 * rms_term * K / sqrt(2); eight
+    standard deviations are allowed."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W, np.float64)
+    K = x.shape[1]
+    rms = np.sqrt(np.maximum((x * x) @ (W * W).T, 0.0) / K)
+    return 8.0 * 2.0 ** -24 * rms * K / np.sqrt(2.0)
+
+
+def check_h_and_down(H_gpu, parts, x, Wg, Wu, Wd, Yp_gpu, o_ref, what=""):
+    """Stage check of the expert FFN where h is rounded to bf16.
+
+    Rounding h to bf16 decides a discrete value from a float.  The GPU's fp32 h differs
+    from the oracle's float64 h by at most dh = |SiLU(g)| du + |u SiLU'(g)| dg + 4 ulp32(h)
+    (du, dg from fp32_dot_error), so every GPU h must be the round-to-nearest-even bf16
+    of some value in [h - dh, h + dh]: equal to the oracle's rounding except near a
+    midpoint, where both neighbours are correct.  Given those h, Yp must equal the
+    oracle's o up to the effect of the differences,
+        |Yp - o| <= |W_down| |H - hq| + 4 sqrt(F) 2^-24 |W_down| |hq|,
+    the second term covering fp32 accumulation over F products.
+    """
+    g, u, h64 = parts["g"], parts["u"], parts["h"]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    dh = (np.abs(g * sig) * fp32_dot_error(x, Wu) + np.abs(u * dsilu) * fp32_dot_error(x, Wg)
+          + 4.0 * 2.0 ** -24 * np.abs(h64))
+    H_gpu = np.asarray(H_gpu, np.float64)
+    hq = oracle.bf16_round(h64.astype(np.float32)).astype(np.float64)
+    lo = oracle.bf16_round((h64 - dh).astype(np.float32)).astype(np.float64)
+    hi = oracle.bf16_round((h64 + dh).astype(np.float32)).astype(np.float64)
+    out = (H_gpu < np.minimum(lo, hi)) | (H_gpu > np.maximum(lo, hi))
+    assert not out.any(), f"{what}: {out.sum()} h values are no rounding of [h-dh, h+dh] " \
+                          f"(e.g. gpu {H_gpu[out][:3]} vs oracle {h64[out][:3]})"
+    diff = H_gpu != hq
+    assert diff.mean() < 1e-2, f"{what}: {diff.mean():.2e} of h values differ"
+    Wd = np.abs(np.asarray(Wd, np.float64))
+    F = Wd.shape[1]
+    bound = np.abs(H_gpu - hq) @ Wd.T + 4.0 * np.sqrt(F) * 2.0 ** -24 * (np.abs(hq) @ Wd.T)
+    err = np.abs(np.asarray(Yp_gpu, np.float64) - o_ref)
+    bad = err > bound + 1e-30
+    assert not bad.any(), f"{what}: {bad.sum()} Yp elements beyond the rounding bound " \
+                          f"(worst excess {(err - bound).max():.3e})"
+    return int(diff.sum())

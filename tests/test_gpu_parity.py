@@ -15,7 +15,7 @@ import gen
 import oracle
 import sparse_mixture_experts_24_amd as moe
 from gen import Workload
-from parity import STAT_TOL, check_routing, check_y, np32, to_dev
+from parity import STAT_TOL, check_h_and_down, check_routing, check_y, np32, to_dev
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -87,23 +87,28 @@ def test_experts_forced_dispatch(case):
                         wl.k, wl.E, want_h=True)
     torch.cuda.synchronize()
     Yp = Yp.cpu().numpy()
-    N = int(d["offsets"][-1])
+    H = H.float().cpu().numpy()
     x = np32(inp["x"])
     hb = wl.dtype == "bf16"
-    rows = []
-    for e in range(wl.E):
-        lo, hi = int(d["offsets"][e]), int(d["offsets"][e + 1])
-        if hi > lo:
-            tok = d["perm_src"][lo:hi] // wl.k
-            rows.append(oracle.expert_ffn(x[tok], np32(inp["W_gate"][e]), np32(inp["W_up"][e]),
-                                          np32(inp["W_down"][e]), hb))
-    if N:
-        check_y(Yp[:N], np.concatenate(rows), f"{name}: routed expert rows")
+    groups = [(e, int(d["offsets"][e]), int(d["offsets"][e + 1]),
+               d["perm_src"][int(d["offsets"][e]):int(d["offsets"][e + 1])] // wl.k)
+              for e in range(wl.E)]
     if wl.n_shared:
-        sh = oracle.expert_ffn(x, np32(inp["W_gate"][wl.E]), np32(inp["W_up"][wl.E]),
-                               np32(inp["W_down"][wl.E]), hb)
         r0 = wl.T * wl.k
-        check_y(Yp[r0:r0 + wl.T], sh, f"{name}: shared expert rows")
+        groups.append((wl.E, r0, r0 + wl.T, np.arange(wl.T)))
+    flips = 0
+    for e, lo, hi, tok in groups:
+        if hi == lo:
+            continue
+        Wg, Wu, Wd = np32(inp["W_gate"][e]), np32(inp["W_up"][e]), np32(inp["W_down"][e])
+        o, parts = oracle.expert_ffn(x[tok], Wg, Wu, Wd, hb, return_h=True)
+        if hb:
+            flips += check_h_and_down(H[lo:hi], parts, x[tok], Wg, Wu, Wd, Yp[lo:hi], o,
+                                      f"{name} expert {e}")
+        else:
+            np.testing.assert_allclose(H[lo:hi], parts["h"], rtol=1e-4, atol=1e-5)
+            check_y(Yp[lo:hi], o, f"{name} expert {e}")
+    print(f"[{name}] bf16 h roundings on the other side of a midpoint: {flips}")
 
 
 def test_combine_forced_inputs(case):
