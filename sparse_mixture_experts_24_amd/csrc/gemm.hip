@@ -29,6 +29,9 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// Native vector type for 16-byte global/LDS moves (HIP's uint4 struct is copied through
+// memory and would keep the staging registers in scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const void* A;          // gated: x [T, K]; down: H [rows, K]
@@ -155,19 +158,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint4 ra[8], rb[8];
+    u32x4 ra[8], rb[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(A + aoff[i]);
-      rb[i] = *reinterpret_cast<const uint4*>((i < 4 ? Bg : Bu) + boff[i]);
+      ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i]);
+      rb[i] = *reinterpret_cast<const u32x4*>((i < 4 ? Bg : Bu) + boff[i]);
     }
     {
       bf16_t* As = smem;
       bf16_t* Bs = smem + BM * LDK;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<uint4*>(As + (lr + 32 * i) * LDK + lc) = ra[i];
-        *reinterpret_cast<uint4*>(Bs + (lr + 32 * i) * LDK + lc) = rb[i];
+        *reinterpret_cast<u32x4*>(As + (lr + 32 * i) * LDK + lc) = ra[i];
+        *reinterpret_cast<u32x4*>(Bs + (lr + 32 * i) * LDK + lc) = rb[i];
       }
     }
     __syncthreads();
@@ -178,8 +181,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int koff = (kt + 1) * BK;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          ra[i] = *reinterpret_cast<const uint4*>(A + aoff[i] + koff);
-          rb[i] = *reinterpret_cast<const uint4*>((i < 4 ? Bg : Bu) + boff[i] + koff);
+          ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + koff);
+          rb[i] = *reinterpret_cast<const u32x4*>((i < 4 ? Bg : Bu) + boff[i] + koff);
         }
       }
       const bf16_t* As = smem + (kt & 1) * STAGE;
@@ -208,8 +211,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         bf16_t* Bs2 = As2 + BM * LDK;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          *reinterpret_cast<uint4*>(As2 + (lr + 32 * i) * LDK + lc) = ra[i];
-          *reinterpret_cast<uint4*>(Bs2 + (lr + 32 * i) * LDK + lc) = rb[i];
+          *reinterpret_cast<u32x4*>(As2 + (lr + 32 * i) * LDK + lc) = ra[i];
+          *reinterpret_cast<u32x4*>(Bs2 + (lr + 32 * i) * LDK + lc) = rb[i];
         }
       }
       __syncthreads();

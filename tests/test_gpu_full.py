@@ -13,7 +13,8 @@ import torch
 import gen
 import oracle
 import sparse_mixture_experts_24_amd as moe
-from parity import STAT_TOL, check_routing, check_y, np32, to_dev
+from parity import (STAT_TOL, check_routing, check_y_rounding_aware, expert_rows_reference,
+                    np32, to_dev)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -68,13 +69,32 @@ def test_full_size(name):
     assert np.array_equal(perm.cpu().numpy()[:N], d_ref["perm_src"])
     assert np.array_equal(slot.cpu().numpy(), d_ref["slot_pos"])
 
+    # The same kernels staged, to read back the bf16 intermediate H the layer used:
+    # route -> dispatch -> experts -> combine must reproduce moe_forward bit for bit.
+    gidx = torch.from_numpy(idx).to(DEV)
+    _, offs_g, perm_g, slot_g = moe.dispatch(gidx, wl.E, wl.capacity_factor)
+    Yp, H = moe.experts(dinp["x"], perm_g, offs_g, dinp["W_gate"], dinp["W_up"],
+                        dinp["W_down"], wl.k, wl.E, want_h=True)
+    y_staged = moe.combine(Yp, slot_g, w, wl.T, wl.d, wl.k, wl.n_shared,
+                           out_dtype=wl.torch_dtype, n_experts=wl.E)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_staged.float().cpu().numpy(), y), "staged path differs from moe_forward"
+    H = H.float().cpu().numpy()
+    del Yp, y_staged
+
     # sampled output rows, with the layer's own (validated) routing
     routing = dict(r, idx=idx, w=oracle.renorm_weights(r["p"], idx))
     d_gpu = oracle.dispatch(idx, wl.E, C)
+    assert np.array_equal(slot_g.cpu().numpy(), d_gpu["slot_pos"])
     rows = sample_rows(wl.T, 16 if wl.T > 64 else wl.T, d_gpu["slot_pos"], wl.k)
     print(f"[full] {name}: oracle experts for {rows.size} rows", flush=True)
+    hb = wl.dtype == "bf16"
     y_ref = oracle.forward_rows(inp, rows, wl.k, wl.capacity_factor, wl.n_shared,
-                                h_bf16=(wl.dtype == "bf16"), routing=routing, disp=d_gpu)
-    check_y(y[rows], y_ref, f"{name}: sampled rows")
+                                h_bf16=hb, routing=routing, disp=d_gpu)
+    y_ref2, items = expert_rows_reference(inp, rows, wl.k, wl.n_shared, hb, routing, d_gpu)
+    np.testing.assert_allclose(y_ref2, y_ref, rtol=1e-6, atol=1e-7)
+    nflip = check_y_rounding_aware(y[rows], y_ref, items, H, hb, hb, f"{name}: sampled rows")
+    print(f"[full] {name}: {nflip} of {y_ref.size} sampled elements needed the bf16-rounding "
+          f"allowance of the per-element rule", flush=True)
     del dinp, layer
     torch.cuda.empty_cache()

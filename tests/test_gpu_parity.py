@@ -150,7 +150,7 @@ def test_forward(case, odt):
         check_routing(idx, w.cpu().numpy(), r)
         ref = oracle.forward(inp, wl.k, wl.capacity_factor, wl.n_shared,
                              h_bf16=(wl.dtype == "bf16"), idx_override=idx)
-    check_y(y, ref["y"], f"{name}: y")
+    check_y(y, ref["y"], f"{name}: y")     # the strict rule holds at these sizes
     np.testing.assert_allclose(f.cpu().numpy(), ref["f"], atol=STAT_TOL, rtol=0)
     np.testing.assert_allclose(p.cpu().numpy(), ref["p"], atol=STAT_TOL, rtol=0)
 
