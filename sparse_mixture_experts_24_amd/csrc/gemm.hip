@@ -55,10 +55,12 @@ __device__ inline void group_rows(const GemmArgs& a, int g, int64_t& row_begin, 
   }
 }
 
-// Builds, in LDS, the exclusive prefix over groups of ceil(M_g / bm) (the m-tile
-// table) from the dispatch offsets; tiles[G] is the total.  Wavefront 0 scans the
+// Builds, in LDS, the exclusive prefix over groups of their m-tile counts (the tile
+// table) from the dispatch offsets; tiles[G] is the total.  A group's tile height is
+// tile_rows(M) (bf16 kernel: by group size; fp32 kernel: fixed).  Wavefront 0 scans the
 // groups 64 at a time.  Ends with a barrier.
-__device__ inline void build_tile_table(const GemmArgs& a, int bm, int* tiles) {
+template <typename RowsFn>
+__device__ inline void build_tile_table(const GemmArgs& a, RowsFn tile_rows, int* tiles) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
@@ -67,6 +69,7 @@ __device__ inline void build_tile_table(const GemmArgs& a, int bm, int* tiles) {
       int c = 0;
       if (g < a.G) {
         const int M = (g < a.E) ? a.offsets[g + 1] - a.offsets[g] : a.T;
+        const int bm = tile_rows(M);
         c = (M + bm - 1) / bm;
       }
       int incl = c;
@@ -102,30 +105,221 @@ __device__ inline int64_t a_source_row(const GemmArgs& a, int g, int64_t row_beg
 }
 
 __device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
+// SiLU with the hardware exp2 and reciprocal (a few ulp of fp32); used where h is then
+// rounded to bf16, whose step is 2^16 times coarser.
+__device__ inline float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8;
-constexpr int STAGE = (BM + BN) * LDK;                       // bf16 elements per stage
-constexpr size_t GEMM_LDS_BYTES = 2 * STAGE * sizeof(bf16_t);  // 147456
+// Output tile BM x BN, BN = 256 (gate/up: 128 gate + the matching 128 up columns).
+// BM = 32*MB rows: 256 for groups of at least SMALL_GROUP_ROWS rows, 64 below that, so
+// small experts (decode, the tail of skewed or capacity-limited routing) do not pay for
+// 256-row MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate
+// + 32 up) and all BM A rows: MB x 2 blocks of 32x32 accumulators.
+//   * B (the weights) goes straight from global memory into MFMA operand registers,
+//     three register sets deep: the set for K-step t+2 is issued at step t, so a weight
+//     load has two steps of work to arrive;
+//   * A (the token rows) is staged once per block through LDS (two stages, rows padded to
+//     72 bf16 so fragment reads hit distinct banks) and read by all four waves;
+//   * inside a 64-wide K step the MFMA k-slots are permuted: step s, lane half g uses the
+//     physical columns [32g + 8s, 32g + 8s + 8), for A and B alike, so each lane's B data
+//     for the whole step is 64 contiguous bytes of one weight row;
+//   * each K step is one scheduling region in which the fragment reads of k16 step s+1
+//     and the global loads are interleaved with the MFMAs of step s.
+constexpr int BN = 256, BK = 64, LDK = BK + 8;
+constexpr int BM_BIG = 256, BM_SMALL = 64, SMALL_GROUP_ROWS = 128;
+constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
+
+__device__ inline int bf16_tile_rows(int M) { return M >= SMALL_GROUP_ROWS ? BM_BIG : BM_SMALL; }
+
+template <int MB, bool GATED>
+__device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
+                                               int64_t row_begin, int M, int m0, int ncol0) {
+  constexpr int BMT = 32 * MB;
+  constexpr int STAGE = BMT * LDK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;       // A load: row lr + 32i, k offset lc
+  const int fr = lane & 31, fg = lane >> 5;          // fragment row / lane half
+  const bf16_t* A = (const bf16_t*)a.A;
+  const int K = a.K, N = a.N;
+  const int nk = K / BK;
+
+  // A: element offsets (32-bit; the host bounds T*d and rows*F below 2^31).  The
+  // perm_src gathers of the routed rows are issued together, then converted.
+  int aoff[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + lr + 32 * i;
+    aoff[i] = m < M ? m : 0;
+  }
+  if (GATED && g < a.E) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = a.perm_src[row_begin + aoff[i]];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = aoff[i] / a.topk * K + lc;
+  } else {
+    const int base = GATED ? 0 : (int)row_begin;     // shared expert: token m; down: row
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = (base + aoff[i]) * K + lc;
+  }
+  // B: this lane's two weight rows (n-block 0 and 1), 32 contiguous k per lane half
+  const bf16_t* pb[2];
+  int bcol[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 64 * w + 32 * nb + fr;
+    const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
+    bcol[nb] = n;
+    pb[nb] = base + ((int64_t)g * N + min(n, N - 1)) * K + 32 * fg;
+  }
+
+  floatx16 acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 b0[2][4], b1[2][4], b2[2][4];   // three B register sets (nb, k16 step)
+  u32x4 ra[MB];
+
+#define MOE_LOAD_B(set, t)                                                                 \
+  _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                         \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
+      set[nb][s] = *reinterpret_cast<const bf16x8*>(pb[nb] + min((t), nk - 1) * BK + 8 * s);
+#define MOE_LOAD_A(t)                                                                      \
+  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
+    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (t) * BK);
+#define MOE_STORE_A(st)                                                                    \
+  {                                                                                        \
+    bf16_t* As_ = smem + (st) * STAGE;                                                     \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
+      *reinterpret_cast<u32x4*>(As_ + (lr + 32 * i) * LDK + lc) = ra[i];                   \
+  }
+#define MOE_READ_A(af, st, s)                                                              \
+  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
+    af[mb] = *reinterpret_cast<const bf16x8*>(smem + (st) * STAGE + (mb * 32 + fr) * LDK + \
+                                              32 * fg + 8 * (s));
+#define MOE_MFMA(af, set, s)                                                               \
+  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
+    _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                       \
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], set[nb][s], acc[mb][nb], \
+                                                            0, 0, 0);
+#define MOE_COMPUTE(set, st)                                                               \
+  {                                                                                        \
+    bf16x8 fa[MB], fb[MB];                                                                 \
+    MOE_READ_A(fa, st, 0);                                                                 \
+    MOE_READ_A(fb, st, 1);                                                                 \
+    MOE_MFMA(fa, set, 0);                                                                  \
+    MOE_READ_A(fa, st, 2);                                                                 \
+    MOE_MFMA(fb, set, 1);                                                                  \
+    MOE_READ_A(fb, st, 3);                                                                 \
+    MOE_MFMA(fa, set, 2);                                                                  \
+    MOE_MFMA(fb, set, 3);                                                                  \
+  }
+  // Region order: the 2*MB fragment reads of k16 steps 0 and 1, then per k16 step s a
+  // quarter of the MB + 8 global loads and MB x {MFMA, (read for s+2), MFMA}.
+#define MOE_INTERLEAVE(s, reads)                                                           \
+  {                                                                                        \
+    constexpr int NGL_ = MB + 8;                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x020, NGL_ * ((s) + 1) / 4 - NGL_ * (s) / 4, 0); \
+    _Pragma("unroll") for (int j_ = 0; j_ < MB; ++j_) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+    }                                                                                      \
+  }
+  // Steps t >= nk (padding the step count up to a multiple of 3) read zero A rows, so the
+  // accumulators are unchanged, and the loop body has no exits.
+#define MOE_STEP(t, cur, nxt2)                                                             \
+  {                                                                                        \
+    MOE_LOAD_A(min((t) + 1, nk - 1));                                                      \
+    MOE_LOAD_B(nxt2, (t) + 2);                                                             \
+    MOE_COMPUTE(cur, (t) & 1);                                                             \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);                                \
+    MOE_INTERLEAVE(0, 1)                                                                   \
+    MOE_INTERLEAVE(1, 1)                                                                   \
+    MOE_INTERLEAVE(2, 0)                                                                   \
+    MOE_INTERLEAVE(3, 0)                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if ((t) + 1 >= nk) {                                                                   \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) ra[i] = u32x4{0u, 0u, 0u, 0u};        \
+    }                                                                                      \
+    MOE_STORE_A(((t) + 1) & 1);                                                            \
+    __syncthreads();                                                                       \
+  }
+
+  MOE_LOAD_B(b0, 0);
+  MOE_LOAD_B(b1, 1);
+  MOE_LOAD_A(0);
+  MOE_STORE_A(0);
+  __syncthreads();
+  const int nk3 = (nk + 2) / 3 * 3;
+  for (int kt = 0; kt < nk3; kt += 3) {
+    MOE_STEP(kt, b0, b2);
+    MOE_STEP(kt + 1, b1, b0);
+    MOE_STEP(kt + 2, b2, b1);
+  }
+#undef MOE_LOAD_B
+#undef MOE_LOAD_A
+#undef MOE_STORE_A
+#undef MOE_READ_A
+#undef MOE_MFMA
+#undef MOE_COMPUTE
+#undef MOE_INTERLEAVE
+#undef MOE_STEP
+
+  // Epilogue.  D[m][n] of a 32x32 block: lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
+  if (GATED) {
+    // h = SiLU(g) * u -> bf16 into an LDS tile [BM][128 + 8], then 16-byte row stores.
+    // (The A stages are free: the last K step ended with a barrier.)
+    constexpr int HLD = 136;
+    bf16_t* Ht = smem;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
+        Ht[row * HLD + 32 * w + fr] = f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][1][r]);
+      }
+    __syncthreads();
+    bf16_t* H = (bf16_t*)a.out;
+#pragma unroll 4
+    for (int i = 0; i < BMT / 16; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, cc = (c & 15) * 8;
+      const int m = m0 + row, n = ncol0 + cc;   // N % 64 == 0: n < N implies n + 8 <= N
+      if (m < M && n < N)
+        *reinterpret_cast<u32x4*>(H + (row_begin + m) * N + n) =
+            *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
+    }
+    __syncthreads();   // the next tile's prologue overwrites the LDS
+  } else {
+    float* Y = (float*)a.out;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = bcol[nb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
+          if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
+        }
+      }
+  }
+}
 
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int lr = tid >> 3, lc = (tid & 7) * 8;   // load row (0..31) and k offset
-  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row and k offset
-  const bf16_t* A = (const bf16_t*)a.A;
-  const bf16_t* B0 = (const bf16_t*)a.B0;
-  const bf16_t* B1 = (const bf16_t*)a.B1;
-  const int K = a.K, N = a.N;
-  const int nk = K / BK;
   __shared__ int tiles[kMaxExperts + 2];
-  build_tile_table(a, BM, tiles);
+  build_tile_table(a, bf16_tile_rows, tiles);   // ends with a barrier
   const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
   const int per = gridDim.x >> 3;
   const int64_t first = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-
   for (int64_t tile = first; tile < total; tile += gridDim.x) {
     const int g = find_group(tiles, a.G, a.n_tiles, tile);
     int64_t row_begin;
@@ -133,122 +327,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     group_rows(a, g, row_begin, M);
     const int mt_g = tiles[g + 1] - tiles[g];
     const int64_t local = tile - (int64_t)tiles[g] * a.n_tiles;
-    const int m0 = (int)(local % mt_g) * BM;
+    const int mt = (int)(local % mt_g);
     const int ncol0 = (int)(local / mt_g) * (GATED ? BN / 2 : BN);
-
-    // Element offsets (32-bit: the host bounds T*d, rows*F and F*d below 2^31) of the 8
-    // A rows and 8 B rows this thread loads.
-    int aoff[8], boff[8];
-    const bf16_t* Bg = B0 + (int64_t)g * N * K;
-    const bf16_t* Bu = GATED ? B1 + (int64_t)g * N * K : Bg;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + lr + 32 * i;
-      aoff[i] = (int)a_source_row<GATED>(a, g, row_begin, m < M ? m : 0) * K + lc;
-      // gated: rows [0,128) of the B tile are gate rows (i < 4), [128,256) up rows
-      const int nl = GATED ? ((lr + 32 * i) & 127) : (lr + 32 * i);
-      boff[i] = min(ncol0 + nl, N - 1) * K + lc;
-    }
-
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    u32x4 ra[8], rb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i]);
-      rb[i] = *reinterpret_cast<const u32x4*>((i < 4 ? Bg : Bu) + boff[i]);
-    }
-    {
-      bf16_t* As = smem;
-      bf16_t* Bs = smem + BM * LDK;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<u32x4*>(As + (lr + 32 * i) * LDK + lc) = ra[i];
-        *reinterpret_cast<u32x4*>(Bs + (lr + 32 * i) * LDK + lc) = rb[i];
-      }
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int koff = (kt + 1) * BK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + koff);
-          rb[i] = *reinterpret_cast<const u32x4*>((i < 4 ? Bg : Bu) + boff[i] + koff);
-        }
-      }
-      const bf16_t* As = smem + (kt & 1) * STAGE;
-      const bf16_t* Bs = As + BM * LDK;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          af[mb] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + mb * 32 + fr) * LDK + ks * 16 + fk);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          int brow;
-          if (GATED) brow = (nb < 2) ? (wn * 64 + nb * 32 + fr) : (128 + wn * 64 + (nb - 2) * 32 + fr);
-          else brow = wn * 128 + nb * 32 + fr;
-          bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + brow * LDK + ks * 16 + fk);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-      }
-      if (more) {
-        bf16_t* As2 = smem + ((kt + 1) & 1) * STAGE;
-        bf16_t* Bs2 = As2 + BM * LDK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          *reinterpret_cast<u32x4*>(As2 + (lr + 32 * i) * LDK + lc) = ra[i];
-          *reinterpret_cast<u32x4*>(Bs2 + (lr + 32 * i) * LDK + lc) = rb[i];
-        }
-      }
-      __syncthreads();
-    }
-
-    // Epilogue.  D[m][n] of a 32x32 block: lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
-    if (GATED) {
-      bf16_t* H = (bf16_t*)a.out;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = ncol0 + wn * 64 + nb * 32 + fr;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < M && n < N) {
-              const float h = silu_f(acc[mb][nb][r]) * acc[mb][nb + 2][r];
-              H[(row_begin + m) * N + n] = f32_to_bf16(h);
-            }
-          }
-        }
-    } else {
-      float* Y = (float*)a.out;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = ncol0 + wn * 128 + nb * 32 + fr;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
-          }
-        }
-    }
+    if (bf16_tile_rows(M) == BM_BIG)
+      gemm_bf16_tile<BM_BIG / 32, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0);
+    else
+      gemm_bf16_tile<BM_SMALL / 32, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
   }
 }
 
@@ -260,7 +344,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   __shared__ float As[TK][TM + 4];
   __shared__ float Bs[GATED ? 2 : 1][TK][TN + 4];
   __shared__ int tiles[kMaxExperts + 2];
-  build_tile_table(a, TM, tiles);
+  build_tile_table(a, [](int) { return 64; }, tiles);   // TM-row tiles
   const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
   const int64_t tile = blockIdx.x;
   if (tile >= total) return;
@@ -389,7 +473,7 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.N = (int)d.d_ff;
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, bf ? BN / 2 : 64);
-  return bf ? run_bf16<true>(a, max_m_tiles(d, BM), s) : run_f32<true>(a, max_m_tiles(d, 64), s);
+  return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL), s) : run_f32<true>(a, max_m_tiles(d, 64), s);
 }
 
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
@@ -402,7 +486,7 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
   a.N = (int)d.d_model;
   a.K = (int)d.d_ff;
   a.n_tiles = (int)ceil_div(d.d_model, bf ? BN : 64);
-  return bf ? run_bf16<false>(a, max_m_tiles(d, BM), s) : run_f32<false>(a, max_m_tiles(d, 64), s);
+  return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL), s) : run_f32<false>(a, max_m_tiles(d, 64), s);
 }
 
 }  // namespace moe
