@@ -23,6 +23,8 @@
 //     the m-tiles that share a weight tile run on the same L2.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,6 +44,7 @@ struct GemmArgs {
   void* out;              // gated: H [rows, N] (dtype); down: Yp [rows, N] fp32
   int64_t shared_row0;    // T*k: first row of the shared expert
   int T, topk, E, G, N, K, n_tiles;
+  int narrow_small;       // down GEMM: 128-column tiles for small groups (few tiles overall)
 };
 
 // Geometry of group g.
@@ -55,23 +58,19 @@ __device__ inline void group_rows(const GemmArgs& a, int g, int64_t& row_begin, 
   }
 }
 
-// Builds, in LDS, the exclusive prefix over groups of their m-tile counts (the tile
-// table) from the dispatch offsets; tiles[G] is the total.  A group's tile height is
-// tile_rows(M) (bf16 kernel: by group size; fp32 kernel: fixed).  Wavefront 0 scans the
-// groups 64 at a time.  Ends with a barrier.
-template <typename RowsFn>
-__device__ inline void build_tile_table(const GemmArgs& a, RowsFn tile_rows, int* tiles) {
+// Builds, in LDS, the exclusive prefix over groups of their tile counts (the tile
+// table) from the dispatch offsets; tiles[G] is the total.  tile_count(M) gives a group's
+// number of tiles from its row count.  Wavefront 0 scans the groups 64 at a time.  Ends
+// with a barrier.
+template <typename CountFn>
+__device__ inline void build_tile_table(const GemmArgs& a, CountFn tile_count, int* tiles) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
     for (int base = 0; base < a.G; base += 64) {
       const int g = base + lane;
       int c = 0;
-      if (g < a.G) {
-        const int M = (g < a.E) ? a.offsets[g + 1] - a.offsets[g] : a.T;
-        const int bm = tile_rows(M);
-        c = (M + bm - 1) / bm;
-      }
+      if (g < a.G) c = tile_count((g < a.E) ? a.offsets[g + 1] - a.offsets[g] : a.T);
       int incl = c;
       for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, 64);
@@ -85,12 +84,12 @@ __device__ inline void build_tile_table(const GemmArgs& a, RowsFn tile_rows, int
   __syncthreads();
 }
 
-// tile -> group; tiles are ordered (group, n-tile, m-tile).
-__device__ inline int find_group(const int* tiles, int G, int n_tiles, int64_t tile) {
-  int lo = 0, hi = G;     // tiles[lo]*n_tiles <= tile < tiles[hi]*n_tiles
+// tile -> group: the g with tiles[g] <= tile < tiles[g + 1] (a group with tiles).
+__device__ inline int find_group(const int* tiles, int G, int64_t tile) {
+  int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)tiles[mid] * n_tiles <= tile) lo = mid;
+    if (tiles[mid] <= tile) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -127,15 +126,25 @@ __device__ inline float silu_fast(float z) {
 //     for the whole step is 64 contiguous bytes of one weight row;
 //   * each K step is one scheduling region in which the fragment reads of k16 step s+1
 //     and the global loads are interleaved with the MFMAs of step s.
-constexpr int BN = 256, BK = 64, LDK = BK + 8;
+constexpr int BK = 64, LDK = BK + 8;
 constexpr int BM_BIG = 256, BM_SMALL = 64, SMALL_GROUP_ROWS = 128;
 constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 
-__device__ inline int bf16_tile_rows(int M) { return M >= SMALL_GROUP_ROWS ? BM_BIG : BM_SMALL; }
+// Tile shape of a group with M rows: 256-row tiles for large groups, 64-row tiles for
+// small ones.  Columns per tile: gate/up 128 (each wave one 32-column block of gate and
+// the same block of up); down 256, or 128 for small groups when the host finds the
+// whole launch short of tiles (decode-sized batches, where the GEMM streams weights and
+// every CU must take part).
+__device__ inline bool small_group(int M) { return M < SMALL_GROUP_ROWS; }
+template <bool GATED>
+__device__ inline int tile_cols(bool small, int narrow_small) {
+  return GATED ? 128 : ((small && narrow_small) ? 128 : 256);
+}
 
-template <int MB, bool GATED>
+template <int MB, int NB, bool GATED>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
                                                int64_t row_begin, int M, int m0, int ncol0) {
+  static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
   constexpr int BMT = 32 * MB;
   constexpr int STAGE = BMT * LDK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -163,30 +172,30 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #pragma unroll
     for (int i = 0; i < MB; ++i) aoff[i] = (base + aoff[i]) * K + lc;
   }
-  // B: this lane's two weight rows (n-block 0 and 1), 32 contiguous k per lane half
-  const bf16_t* pb[2];
-  int bcol[2];
+  // B: this lane's NB weight rows (one per n-block), 32 contiguous k per lane half
+  const bf16_t* pb[NB];
+  int bcol[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 64 * w + 32 * nb + fr;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
     const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
     bcol[nb] = n;
     pb[nb] = base + ((int64_t)g * N + min(n, N - 1)) * K + 32 * fg;
   }
 
-  floatx16 acc[MB][2];
+  floatx16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8 b0[2][4], b1[2][4], b2[2][4];   // three B register sets (nb, k16 step)
+  bf16x8 b0[NB][4], b1[NB][4], b2[NB][4];   // three B register sets (nb, k16 step)
   u32x4 ra[MB];
 
 #define MOE_LOAD_B(set, t)                                                                 \
-  _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                         \
+  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                        \
     _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
       set[nb][s] = *reinterpret_cast<const bf16x8*>(pb[nb] + min((t), nk - 1) * BK + 8 * s);
 #define MOE_LOAD_A(t)                                                                      \
@@ -204,7 +213,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
                                               32 * fg + 8 * (s));
 #define MOE_MFMA(af, set, s)                                                               \
   _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
-    _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                       \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                      \
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], set[nb][s], acc[mb][nb], \
                                                             0, 0, 0);
 #define MOE_COMPUTE(set, st)                                                               \
@@ -220,15 +229,14 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     MOE_MFMA(fb, set, 3);                                                                  \
   }
   // Region order: the 2*MB fragment reads of k16 steps 0 and 1, then per k16 step s a
-  // quarter of the MB + 8 global loads and MB x {MFMA, (read for s+2), MFMA}.
+  // quarter of the MB + 4*NB global loads and MB x {NB MFMAs, (read for step s+2)}.
 #define MOE_INTERLEAVE(s, reads)                                                           \
   {                                                                                        \
-    constexpr int NGL_ = MB + 8;                                                           \
+    constexpr int NGL_ = MB + 4 * NB;                                                      \
     __builtin_amdgcn_sched_group_barrier(0x020, NGL_ * ((s) + 1) / 4 - NGL_ * (s) / 4, 0); \
     _Pragma("unroll") for (int j_ = 0; j_ < MB; ++j_) {                                    \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);                                  \
       if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
   }
   // Steps t >= nk (padding the step count up to a multiple of 3) read zero A rows, so the
@@ -301,7 +309,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const int n = bcol[nb];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -316,23 +324,32 @@ template <bool GATED>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
-  build_tile_table(a, bf16_tile_rows, tiles);   // ends with a barrier
-  const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
+  const int N = a.N, narrow = a.narrow_small;
+  auto tile_count = [N, narrow](int M) {
+    const bool sm = small_group(M);
+    const int bm = sm ? BM_SMALL : BM_BIG, bn = tile_cols<GATED>(sm, narrow);
+    return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  };
+  build_tile_table(a, tile_count, tiles);   // ends with a barrier
+  const int64_t total = tiles[a.G];
   const int per = gridDim.x >> 3;
   const int64_t first = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
   for (int64_t tile = first; tile < total; tile += gridDim.x) {
-    const int g = find_group(tiles, a.G, a.n_tiles, tile);
+    const int g = find_group(tiles, a.G, tile);
     int64_t row_begin;
     int M;
     group_rows(a, g, row_begin, M);
-    const int mt_g = tiles[g + 1] - tiles[g];
-    const int64_t local = tile - (int64_t)tiles[g] * a.n_tiles;
-    const int mt = (int)(local % mt_g);
-    const int ncol0 = (int)(local / mt_g) * (GATED ? BN / 2 : BN);
-    if (bf16_tile_rows(M) == BM_BIG)
-      gemm_bf16_tile<BM_BIG / 32, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0);
-    else
-      gemm_bf16_tile<BM_SMALL / 32, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
+    const bool sm = small_group(M);
+    const int mt_g = (M + (sm ? BM_SMALL : BM_BIG) - 1) / (sm ? BM_SMALL : BM_BIG);
+    const int local = (int)(tile - tiles[g]);          // ordered (n-tile, m-tile)
+    const int mt = local % mt_g;
+    const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
+    if (!sm)
+      gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0);
+    else if (GATED || !narrow)
+      gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
+    else if constexpr (!GATED)
+      gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
   }
 }
 
@@ -344,16 +361,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   __shared__ float As[TK][TM + 4];
   __shared__ float Bs[GATED ? 2 : 1][TK][TN + 4];
   __shared__ int tiles[kMaxExperts + 2];
-  build_tile_table(a, [](int) { return 64; }, tiles);   // TM-row tiles
-  const int64_t total = (int64_t)tiles[a.G] * a.n_tiles;
+  const int nt = a.n_tiles;
+  build_tile_table(a, [nt](int M) { return (M + 63) / 64 * nt; }, tiles);   // 64 x 64 tiles
+  const int64_t total = tiles[a.G];
   const int64_t tile = blockIdx.x;
   if (tile >= total) return;
-  const int g = find_group(tiles, a.G, a.n_tiles, tile);
+  const int g = find_group(tiles, a.G, tile);
   int64_t row_begin;
   int M;
   group_rows(a, g, row_begin, M);
-  const int mt_g = tiles[g + 1] - tiles[g];
-  const int64_t local = tile - (int64_t)tiles[g] * a.n_tiles;
+  const int mt_g = (M + 63) / 64;
+  const int64_t local = tile - tiles[g];
   const int m0 = (int)(local % mt_g) * TM;
   const int n0 = (int)(local / mt_g) * TN;
   const float* A = (const float*)a.A;
@@ -418,7 +436,7 @@ static int device_cu_count() {
 }
 
 template <bool GATED>
-static hipError_t run_bf16(const GemmArgs& a, int64_t max_m_tiles, hipStream_t s) {
+static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED>,
@@ -427,9 +445,8 @@ static hipError_t run_bf16(const GemmArgs& a, int64_t max_m_tiles, hipStream_t s
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t upper = max_m_tiles * a.n_tiles;
   int64_t grid = device_cu_count();
-  if (upper < grid) grid = upper;
+  if (max_tiles < grid) grid = max_tiles;
   grid = round_up(grid, 8);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(gemm_bf16_kernel<GATED>, dim3((unsigned)grid), dim3(256), GEMM_LDS_BYTES, s, a);
@@ -472,8 +489,9 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.out = H;
   a.N = (int)d.d_ff;
   a.K = (int)d.d_model;
-  a.n_tiles = (int)ceil_div(d.d_ff, bf ? BN / 2 : 64);
-  return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL), s) : run_f32<true>(a, max_m_tiles(d, 64), s);
+  a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
+  return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128), s)
+            : run_f32<true>(a, max_m_tiles(d, 64), s);
 }
 
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
@@ -485,8 +503,15 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
   a.out = Yp;
   a.N = (int)d.d_model;
   a.K = (int)d.d_ff;
-  a.n_tiles = (int)ceil_div(d.d_model, bf ? BN : 64);
-  return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL), s) : run_f32<false>(a, max_m_tiles(d, 64), s);
+  a.n_tiles = (int)ceil_div(d.d_model, 64);
+  {
+    // narrow down tiles for small groups only when even the most groups that can exist
+    // would give fewer than two 256-column tiles per CU
+    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, d.T * d.top_k + d.n_shared);
+    a.narrow_small = groups * ceil_div(d.d_model, 256) < 2 * (int64_t)device_cu_count();
+  }
+  return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128), s)
+            : run_f32<false>(a, max_m_tiles(d, 64), s);
 }
 
 }  // namespace moe

@@ -124,7 +124,9 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   hipStream_t s = (hipStream_t)stream;
   const RoutePlan rp = route_plan(d);
   MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, w.p_part, w.cnt_part, s));
-  MOE_HIP(launch_stats(d, w.p_part, w.cnt_part, rp.n_blocks, f, p, s));
+  if (f || p)
+    MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
+                               (int)d.top_k, w.counts, f, p, s));
   return MOE_OK;
 }
 
@@ -143,9 +145,10 @@ moe_status_t moe_dispatch(const moe_desc_t* desc, const int32_t* topk_idx, int32
   const int E = (int)d.n_experts;
   const int64_t C = capacity_of(d);
   MOE_HIP(launch_hist(topk_idx, TK, E, kDispatchChunk, w.cnt_part, s));
-  MOE_HIP(launch_scan(w.cnt_part, ceil_div(TK, kDispatchChunk), E, C, counts, offsets, s));
-  MOE_HIP(launch_scatter(topk_idx, TK, E, kDispatchChunk, C, w.cnt_part, offsets, perm_src,
-                         slot_pos, s));
+  MOE_HIP(launch_expert_scan(w.cnt_part, ceil_div(TK, kDispatchChunk), E, nullptr, d.T,
+                             (int)d.top_k, counts, nullptr, nullptr, s));
+  MOE_HIP(launch_scatter(topk_idx, TK, E, kDispatchChunk, C, w.cnt_part, counts, offsets,
+                         perm_src, slot_pos, s));
   return MOE_OK;
 }
 
@@ -225,10 +228,10 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
   const int64_t C = capacity_of(d);
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
   MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, w.p_part, w.cnt_part, s));
-  MOE_HIP(launch_stats(d, w.p_part, w.cnt_part, rp.n_blocks, f, p, s));
-  MOE_HIP(launch_scan(w.cnt_part, rp.n_blocks, E, C, w.counts, w.offsets, s));
-  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.offsets, w.perm_src,
-                         w.slot_pos, s));
+  MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
+                             f, p, s));
+  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
+                         w.perm_src, w.slot_pos, s));
   MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, s));
   MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, s));
   MOE_HIP(launch_combine(d, w.Yp, w.slot_pos, w.topk_w, out, s));

@@ -57,15 +57,13 @@ constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* p_part,
                         int32_t* cnt_part, hipStream_t s);
-hipError_t launch_stats(const moe_desc_t& d, const float* p_part, const int32_t* cnt_part,
-                        int64_t n_blocks, float* f, float* p, hipStream_t s);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
-hipError_t launch_scan(int32_t* blk_cnt, int64_t n_blocks, int E, int64_t C, int32_t* counts,
-                       int32_t* offsets, hipStream_t s);
+hipError_t launch_expert_scan(int32_t* blk, int64_t nb, int E, const float* p_part, int64_t T,
+                              int k, int32_t* counts, float* f, float* p, hipStream_t s);
 hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int64_t C,
-                          const int32_t* blk_base, const int32_t* offsets, int32_t* perm_src,
-                          int32_t* slot_pos, hipStream_t s);
+                          const int32_t* blk_base, const int32_t* counts, int32_t* offsets,
+                          int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
                           const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
                           hipStream_t s);

@@ -138,7 +138,7 @@ __device__ inline void route_block_stats(const float* psum, float (*pw)[E_PAD], 
   }
 }
 
-template <int EPW, int TPW, int KS>
+template <int EPW, int TPW, int KS, int U>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -177,33 +177,52 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 #pragma unroll
     for (int eb = 0; eb < EPW; ++eb) acc[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // This wave's 64-wide k chunks are c = ks + KS*j, j < nj.  They are processed in
+  // batches of U chunks with two register buffers: the loads of batch b+1 are in flight
+  // while the MFMAs of batch b run.  Chunks past the end load a valid address and a zero
+  // B fragment, so the batch loop needs no exits.
   const int nchunk = d / 64;
-  for (int c = ks; c < nchunk; c += KS) {
-    bf16x8 a0[TPW], a1[TPW], b0[EPW], b1[EPW];
-#pragma unroll
-    for (int tb = 0; tb < TPW; ++tb) {
-      const bf16x8* pa = reinterpret_cast<const bf16x8*>(arow[tb] + c * 64);
-      a0[tb] = pa[0];
-      a1[tb] = pa[1];
-    }
-#pragma unroll
-    for (int eb = 0; eb < EPW; ++eb) {
-      const bf16x8* pb = reinterpret_cast<const bf16x8*>(brow[eb] + c * 64);
-      b0[eb] = pb[0];
-      b1[eb] = pb[1];
-      if (!bok[eb]) {
-        b0[eb] = bf16x8{};
-        b1[eb] = bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int tb = 0; tb < TPW; ++tb)
-#pragma unroll
-      for (int eb = 0; eb < EPW; ++eb) {
-        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[tb], b0[eb], acc[tb][eb], 0, 0, 0);
-        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[tb], b1[eb], acc[tb][eb], 0, 0, 0);
-      }
+  const int nj = (nchunk - ks + KS - 1) / KS;
+  const int nbatch = (nj + U - 1) / U;
+  bf16x8 xa[2][U][TPW][2], xb[2][U][EPW][2];
+#define R_LOAD(BUF, batch)                                                                  \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                           \
+    const int j_ = (batch) * U + u;                                                         \
+    const bool live_ = j_ < nj;                                                             \
+    const int c_ = ks + KS * min(j_, nj - 1);                                               \
+    _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb) {                                    \
+      const bf16x8* pa = reinterpret_cast<const bf16x8*>(arow[tb] + c_ * 64);               \
+      xa[BUF][u][tb][0] = pa[0];                                                            \
+      xa[BUF][u][tb][1] = pa[1];                                                            \
+    }                                                                                       \
+    _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb) {                                    \
+      const bf16x8* pb = reinterpret_cast<const bf16x8*>(brow[eb] + c_ * 64);               \
+      xb[BUF][u][eb][0] = pb[0];                                                            \
+      xb[BUF][u][eb][1] = pb[1];                                                            \
+      if (!(bok[eb] && live_)) {                                                            \
+        xb[BUF][u][eb][0] = bf16x8{};                                                       \
+        xb[BUF][u][eb][1] = bf16x8{};                                                       \
+      }                                                                                     \
+    }                                                                                       \
   }
+#define R_MFMA(BUF)                                                                         \
+  _Pragma("unroll") for (int u = 0; u < U; ++u)                                             \
+    _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                      \
+      _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                    \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h)                                       \
+          acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                            \
+              xa[BUF][u][tb][h], xb[BUF][u][eb][h], acc[tb][eb], 0, 0, 0);
+  if (nj > 0) {
+    R_LOAD(0, 0);
+    for (int b = 0; b < nbatch; b += 2) {
+      R_LOAD(1, b + 1);
+      R_MFMA(0);
+      R_LOAD(0, b + 2);
+      R_MFMA(1);
+    }
+  }
+#undef R_LOAD
+#undef R_MFMA
   // D[m][n] of a 16x16 MFMA block sits in lane n + 16*(m/4), register m%4.
 #pragma unroll
   for (int tb = 0; tb < TPW; ++tb)
@@ -326,10 +345,12 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   }
   const bf16_t* xx = (const bf16_t*)x;
   const bf16_t* ww = (const bf16_t*)W_router;
+// U: k chunks per batch, as many as two register buffers of fragments allow.
 #define MOE_ROUTE_BF16(EPW_, TPW_, KS_)                                                      \
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
-    hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_>), grid, block, 0, s, xx, ww, bias, \
-                       T, dm, E, k, topk_idx, topk_w, p_part, cnt_part);                      \
+    constexpr int U_ = (EPW_ + TPW_) <= 2 ? 4 : ((EPW_ + TPW_) <= 4 ? 2 : 1);                 \
+    hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, U_>), grid, block, 0, s, xx, ww,   \
+                       bias, T, dm, E, k, topk_idx, topk_w, p_part, cnt_part);                \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTE_BF16(1, 1, 4)
@@ -343,31 +364,6 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   MOE_ROUTE_BF16(8, 1, 1)
 #undef MOE_ROUTE_BF16
   return hipErrorInvalidValue;
-}
-
-// f_e = sum_b cnt_part[b][e] / (T k);  P_e = sum_b p_part[b][e] / T   (fixed order)
-__global__ void stats_kernel(const float* __restrict__ p_part, const int32_t* __restrict__ cnt_part,
-                             int64_t n_blocks, int E, int64_t T, int k, float* __restrict__ f,
-                             float* __restrict__ p) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
-  float ps = 0.0f;
-  int64_t c = 0;
-  for (int64_t b = 0; b < n_blocks; ++b) {
-    ps += p_part[b * E + e];
-    c += cnt_part[b * E + e];
-  }
-  if (f) f[e] = T > 0 ? (float)((double)c / (double)(T * k)) : 0.0f;
-  if (p) p[e] = T > 0 ? (float)((double)ps / (double)T) : 0.0f;
-}
-
-hipError_t launch_stats(const moe_desc_t& d, const float* p_part, const int32_t* cnt_part,
-                        int64_t n_blocks, float* f, float* p, hipStream_t s) {
-  if (!f && !p) return hipSuccess;
-  const int E = (int)d.n_experts;
-  hipLaunchKernelGGL(stats_kernel, dim3((unsigned)ceil_div(E, 256)), dim3(256), 0, s, p_part,
-                     cnt_part, n_blocks, E, d.T, (int)d.top_k, f, p);
-  return hipGetLastError();
 }
 
 }  // namespace moe
