@@ -140,8 +140,11 @@ def main():
                                      for s in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
     log("[bench] stages (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in stage_ms.items()))
-    same = torch.equal(out, out2)
-    log(f"[bench] staged output identical to moe_forward: {same}")
+    # moe_forward may split the down projection's K range (two fp32 partials), so the
+    # staged output agrees with it to rounding, not bit for bit.
+    dmax = (out.float() - out2.float()).abs().max().item() if out.numel() else 0.0
+    ymax = out.float().abs().max().item() if out.numel() else 0.0
+    log(f"[bench] staged output vs moe_forward: max|diff| {dmax:.3e} (max|y| {ymax:.3e})")
 
     # ---- realised routing -> algorithmic work
     cnt = counts.cpu().numpy().astype(np.int64)

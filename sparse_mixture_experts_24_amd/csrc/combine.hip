@@ -23,8 +23,10 @@ __device__ inline void store4<bf16_t>(bf16_t* out, int64_t i, float4 v) {
   *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
 }
 
+// Yp2 (optional): second partial of a K-split down GEMM; a slot's output is Yp + Yp2.
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp,
+                                                      const float* __restrict__ Yp2,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ w, int T, int k,
                                                       int d, int shared, OutT* __restrict__ out) {
@@ -42,7 +44,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int j = 0; j < k; ++j) {
       const int pos = sp[j];
       if (pos < 0) continue;
-      const float4 v = *reinterpret_cast<const float4*>(Yp + (int64_t)pos * d + c);
+      float4 v = *reinterpret_cast<const float4*>(Yp + (int64_t)pos * d + c);
+      if (Yp2) {
+        const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + (int64_t)pos * d + c);
+        v.x += v2.x;
+        v.y += v2.y;
+        v.z += v2.z;
+        v.w += v2.w;
+      }
       const float wj = sw[j];
       acc.x = fmaf(wj, v.x, acc.x);
       acc.y = fmaf(wj, v.y, acc.y);
@@ -50,7 +59,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc.w = fmaf(wj, v.w, acc.w);
     }
     if (shared) {
-      const float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
+      float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
+      if (Yp2) {
+        const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + srow * d + c);
+        v.x += v2.x;
+        v.y += v2.y;
+        v.z += v2.z;
+        v.w += v2.w;
+      }
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -60,16 +76,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
-                          const float* topk_w, void* out, hipStream_t s) {
+hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
+                          const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   const dim3 grid((unsigned)d.T), block(256);
   const int T = (int)d.T, k = (int)d.top_k, dm = (int)d.d_model, sh = (int)d.n_shared;
   if (d.out_dtype == MOE_DTYPE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, Yp, slot_pos, topk_w, T, k, dm,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, Yp, Yp2, slot_pos, topk_w, T, k, dm,
                        sh, (float*)out);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s, Yp, slot_pos, topk_w, T, k, dm,
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s, Yp, Yp2, slot_pos, topk_w, T, k, dm,
                        sh, (bf16_t*)out);
   return hipGetLastError();
 }

@@ -45,6 +45,8 @@ struct GemmArgs {
   int64_t shared_row0;    // T*k: first row of the shared expert
   int T, topk, E, G, N, K, n_tiles;
   int narrow_small;       // down GEMM: 128-column tiles for small groups (few tiles overall)
+  int ksplit;             // 1, or 2: the K range in two halves, partial sums to out / out2
+  void* out2;             // second partial output (ksplit == 2)
 };
 
 // Geometry of group g.
@@ -141,18 +143,19 @@ __device__ inline int tile_cols(bool small, int narrow_small) {
   return GATED ? 128 : ((small && narrow_small) ? 128 : 256);
 }
 
+// One output tile over K steps [k0, k0 + nk) (the whole K unless split), into outp.
 template <int MB, int NB, bool GATED>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
-                                               int64_t row_begin, int M, int m0, int ncol0) {
+                                               int64_t row_begin, int M, int m0, int ncol0,
+                                               int k0, int nk, void* outp) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
   constexpr int BMT = 32 * MB;
   constexpr int STAGE = BMT * LDK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = tid >> 3, lc = (tid & 7) * 8;       // A load: row lr + 32i, k offset lc
   const int fr = lane & 31, fg = lane >> 5;          // fragment row / lane half
-  const bf16_t* A = (const bf16_t*)a.A;
+  const bf16_t* A = (const bf16_t*)a.A + k0 * BK;
   const int K = a.K, N = a.N;
-  const int nk = K / BK;
 
   // A: element offsets (32-bit; the host bounds T*d and rows*F below 2^31).  The
   // perm_src gathers of the routed rows are issued together, then converted.
@@ -180,7 +183,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
     const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
     bcol[nb] = n;
-    pb[nb] = base + ((int64_t)g * N + min(n, N - 1)) * K + 32 * fg;
+    pb[nb] = base + ((int64_t)g * N + min(n, N - 1)) * K + 32 * fg + k0 * BK;
   }
 
   floatx16 acc[MB][NB];
@@ -293,7 +296,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
         Ht[row * HLD + 32 * w + fr] = f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][1][r]);
       }
     __syncthreads();
-    bf16_t* H = (bf16_t*)a.out;
+    bf16_t* H = (bf16_t*)outp;
 #pragma unroll 4
     for (int i = 0; i < BMT / 16; ++i) {
       const int c = tid + 256 * i;
@@ -305,7 +308,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     }
     __syncthreads();   // the next tile's prologue overwrites the LDS
   } else {
-    float* Y = (float*)a.out;
+    float* Y = (float*)outp;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -331,10 +334,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   };
   build_tile_table(a, tile_count, tiles);   // ends with a barrier
-  const int64_t total = tiles[a.G];
+  const int64_t ntile = tiles[a.G];
+  const int64_t total = ntile * a.ksplit;    // work units: (K half, tile)
+  const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
   const int per = gridDim.x >> 3;
   const int64_t first = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  for (int64_t tile = first; tile < total; tile += gridDim.x) {
+  for (int64_t unit = first; unit < total; unit += gridDim.x) {
+    const int ks = (int)(unit / ntile);
+    const int64_t tile = unit - ks * ntile;
+    const int k0 = ks * nk_half, nk = min(nk_half, nk_all - k0);
+    void* outp = ks == 0 ? a.out : a.out2;
     const int g = find_group(tiles, a.G, tile);
     int64_t row_begin;
     int M;
@@ -345,11 +354,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int mt = local % mt_g;
     const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
     if (!sm)
-      gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0);
+      gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
+                                            nk, outp);
     else if (GATED || !narrow)
-      gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
+      gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+                                              k0, nk, outp);
     else if constexpr (!GATED)
-      gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0);
+      gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+                                              k0, nk, outp);
   }
 }
 
@@ -490,12 +502,29 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.N = (int)d.d_ff;
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
+  a.ksplit = 1;
   return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128), s)
             : run_f32<true>(a, max_m_tiles(d, 64), s);
 }
 
+// Whether moe_forward splits the down GEMM's K range in two: when the estimated number
+// of 256 x 256 output tiles leaves the last round of a 256-CU chip at most 3/4 full and
+// doubling the work units saves at least a quarter of a round.  Host-only arithmetic
+// (no device query), so the workspace size depends on the description alone.
+bool down_split_k(const moe_desc_t& d) {
+  if (d.dtype != MOE_DTYPE_BF16 || d.d_ff / BK < 2) return false;
+  const int64_t TK = d.T * d.top_k;
+  if (TK == 0) return false;
+  const int64_t m_tiles = ceil_div(TK, BM_BIG) + std::min<int64_t>(d.n_experts, TK) +
+                          (d.n_shared ? ceil_div(d.T, BM_BIG) : 0);
+  const int64_t est = m_tiles * ceil_div(d.d_model, 256), cus = 256;
+  if (est > 8 * cus) return false;
+  const double r1 = (double)ceil_div(est, cus), r2 = 0.5 * (double)ceil_div(2 * est, cus);
+  return r2 <= r1 - 0.25;
+}
+
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, hipStream_t s) {
+                       const void* W_down, float* Yp, float* Yp2, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, offsets);
   a.A = H;
@@ -510,6 +539,8 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
     const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, d.T * d.top_k + d.n_shared);
     a.narrow_small = groups * ceil_div(d.d_model, 256) < 2 * (int64_t)device_cu_count();
   }
+  a.ksplit = (bf && Yp2) ? 2 : 1;
+  a.out2 = Yp2;
   return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128), s)
             : run_f32<false>(a, max_m_tiles(d, 64), s);
 }

@@ -56,13 +56,18 @@ Workspace carve_workspace(const moe_desc_t& d, void* base) {
   w.slot_pos = (int32_t*)take(TK * 4);
   w.H = take((size_t)rows * d.d_ff * esz);
   w.Yp = (float*)take((size_t)rows * d.d_model * 4);
-  w.bytes = off;
+  w.bytes = off;   // the minimum; monotone in T
+  // Optional tail: the second partial of a split down GEMM, used when the workspace has
+  // room for it (moe_workspace_bytes asks for it).
+  w.Yp2 = down_split_k(d) ? (float*)take((size_t)rows * d.d_model * 4) : nullptr;
+  w.bytes_full = off;
   return w;
 }
 
 static moe_status_t check_ws(const moe_desc_t& d, void* ws, size_t bytes, Workspace& w) {
   w = carve_workspace(d, ws);
   if (!ws || bytes < w.bytes || ((uintptr_t)ws & 255u)) return MOE_E_WORKSPACE;
+  if (bytes < w.bytes_full) w.Yp2 = nullptr;
   return MOE_OK;
 }
 
@@ -102,7 +107,7 @@ moe_status_t moe_validate(const moe_desc_t* desc) { return validate(desc); }
 
 size_t moe_workspace_bytes(const moe_desc_t* desc) {
   if (validate(desc) != MOE_OK) return 0;
-  return carve_workspace(*desc, nullptr).bytes;
+  return carve_workspace(*desc, nullptr).bytes_full;
 }
 
 int64_t moe_capacity(const moe_desc_t* desc) {
@@ -170,7 +175,7 @@ moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* p
   hipStream_t s = (hipStream_t)stream;
   void* h = H ? H : w.H;
   MOE_HIP(launch_gate_up(d, x, perm_src, offsets, W_gate, W_up, h, s));
-  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, s));
+  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, nullptr, s));
   return MOE_OK;
 }
 
@@ -193,7 +198,7 @@ moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32
   if (st != MOE_OK) return st;
   if (!offsets || !W_down || (desc->T > 0 && (!H || !Yp))) return MOE_E_NULL;
   if (!aligned16(H) || !aligned16(W_down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, (hipStream_t)stream));
+  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, nullptr, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -204,7 +209,7 @@ moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t*
   const moe_desc_t& d = *desc;
   if (d.T > 0 && (!Yp || !slot_pos || !topk_w || !out)) return MOE_E_NULL;
   if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_combine(d, Yp, slot_pos, topk_w, out, (hipStream_t)stream));
+  MOE_HIP(launch_combine(d, Yp, nullptr, slot_pos, topk_w, out, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -233,8 +238,8 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
   MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
                          w.perm_src, w.slot_pos, s));
   MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, s));
-  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, s));
-  MOE_HIP(launch_combine(d, w.Yp, w.slot_pos, w.topk_w, out, s));
+  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, w.Yp2, s));
+  MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
   return MOE_OK;
 }
 

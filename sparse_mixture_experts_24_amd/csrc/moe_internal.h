@@ -47,7 +47,9 @@ struct Workspace {
   int32_t* slot_pos;   // [T*k]
   void* H;             // [T*k + S*T, F] dtype
   float* Yp;           // [T*k + S*T, d]
-  size_t bytes;
+  float* Yp2;          // second partial of the split down GEMM, or NULL
+  size_t bytes;        // minimum size (without Yp2)
+  size_t bytes_full;   // with Yp2 when the layer splits its down GEMM
 };
 Workspace carve_workspace(const moe_desc_t& d, void* base);
 
@@ -67,9 +69,12 @@ hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int6
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
                           const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
                           hipStream_t s);
+// Yp2 non-NULL (bf16 layers): K split in two, partial sums in Yp and Yp2.
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, hipStream_t s);
-hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
-                          const float* topk_w, void* out, hipStream_t s);
+                       const void* W_down, float* Yp, float* Yp2, hipStream_t s);
+bool down_split_k(const moe_desc_t& d);
+// Yp2 non-NULL: the per-slot outputs are Yp + Yp2.
+hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
+                          const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s);
 
 }  // namespace moe

@@ -119,7 +119,7 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     assert L.moe_combine(ctypes.byref(bad), fake, fake, fake, fake, None) == 2
     # workspace missing, too small or misaligned
     assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, None, ws_need, None) == 4
-    assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need - 1, None) == 4
+    assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need // 4, None) == 4
     assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, P(0x100010), ws_need, None) == 4
     assert L.moe_dispatch(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 0, None) == 4
     # misaligned tensors
