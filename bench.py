@@ -41,7 +41,15 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) into the traffic record of --workload; no GPU use")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this layer is built and timed on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
@@ -174,7 +182,7 @@ def main():
         roof = {"bound": "alu", "achieved": flops_gate_up / gu_s / 1e12,
                 "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name)
     roof["kernel"] = "gemm_bf16_kernel<true> (gate/up + SiLU*mul)" if wl.dtype == "bf16" else \
         "gemm_f32_kernel<true>"
     roof["kernel_ms"] = stage_ms["gate_up"]
@@ -208,6 +216,82 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+    if args.copy_calibration:
+        # A plain streaming copy of known size (one elementwise dispatch that reads and
+        # writes COPY_BYTES), for scaling the HBM byte counters.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {COPY_BYTES} bytes read and written")
+
+
+# ---- HBM traffic of the dominant kernel, from rocprofv3 counters
+COPY_BYTES = 1 << 30
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+GEMM_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_24_amd", "csrc", f)
+                for f in ("gemm.hip", "moe_internal.h")]
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up kernel from the committed counter record, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def summarize_pmc(workload, fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the gate/up kernel and of the 1 GiB copy,
+    the copy's ratios known/counted as scale factors, written to profiles/."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: list(v.values()) for k, v in vals.items()}
+
+    def pick(d, pred):
+        names = [k for k in d if pred(k)]
+        if not names:
+            raise SystemExit(f"no matching kernel among {sorted(d)}")
+        return statistics.median([v for k in names for v in d[k]])
+
+    is_gemm = lambda k: "gemm_bf16_kernel<true>" in k or "gemm_bf16_kernelILb1E" in k
+    is_copy = lambda k: "MulFunctor" in k
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    gf, gw = pick(f, is_gemm), pick(w, is_gemm)
+    cf, cw = pick(f, is_copy), pick(w, is_copy)
+    sf, sw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    rec = {"workload": workload, "kernel": "gemm_bf16_kernel<true> (gate/up + SiLU*mul)",
+           "source_sha256": gemm_source_hash(),
+           "fetch_kib_per_launch": gf, "write_kib_per_launch": gw,
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": sf, "write_scale": sw,
+           "hbm_bytes_per_launch": gf * 1024.0 * sf + gw * 1024.0 * sw}
+    out = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(wl, inp, sample):
