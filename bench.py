@@ -126,8 +126,10 @@ def main():
         ("dispatch", lambda: L.moe_dispatch(dref, P(idx), P(counts), P(offsets), P(perm),
                                             P(slot), P(ws), ws.numel(), sp)),
         ("gate_up", lambda: L.moe_experts_gate_up(dref, P(dinp["x"]), P(perm), P(offsets),
-                                                  P(dinp["W_gate"]), P(dinp["W_up"]), P(H), sp)),
-        ("down", lambda: L.moe_experts_down(dref, P(H), P(offsets), P(dinp["W_down"]), P(Yp), sp)),
+                                                  P(dinp["W_gate"]), P(dinp["W_up"]), P(H),
+                                                  P(ws), ws.numel(), sp)),
+        ("down", lambda: L.moe_experts_down(dref, P(H), P(offsets), P(dinp["W_down"]), P(Yp),
+                                            P(ws), ws.numel(), sp)),
         ("combine", lambda: L.moe_combine(dref, P(Yp), P(slot), P(w), P(out2), sp)),
     ]
     for _ in range(max(1, args.warmup)):

@@ -155,13 +155,17 @@ moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* p
  *   moe_experts_gate_up:  H = SiLU(X W_gate^T) * (X W_up^T) on the grouped rows
  *                         (H [T*k + S*T, F] in dtype; rows outside the groups untouched)
  *   moe_experts_down:     Yp = H W_down^T on the same rows (Yp [T*k + S*T, d] float32)
- * Row/group layout as for moe_experts.  Neither needs a workspace.
- * Errors: MOE_E_NULL (any pointer), MOE_E_SHAPE, MOE_E_UNSUPPORTED, MOE_E_HIP. */
+ * Row/group layout as for moe_experts.  The workspace is optional: with one (sized as for
+ * moe_forward) the output tiles are handed out to the CUs dynamically through a few
+ * counters kept in it, without (NULL) in a fixed order; the results are identical.
+ * Errors: MOE_E_NULL (any pointer), MOE_E_SHAPE, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE
+ * (a workspace given but too small or misaligned), MOE_E_HIP. */
 moe_status_t moe_experts_gate_up(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
                                  const int32_t* offsets, const void* W_gate, const void* W_up,
-                                 void* H, void* stream);
+                                 void* H, void* workspace, size_t workspace_bytes, void* stream);
 moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32_t* offsets,
-                              const void* W_down, float* Yp, void* stream);
+                              const void* W_down, float* Yp, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Weighted combine back to token order ("Chapter 30", 30.6.1 and 30.4.5):
  *   out[t] = sum_{j ascending, slot_pos[t*k+j] >= 0} topk_w[t,j] * Yp[slot_pos[t*k+j]]

@@ -75,9 +75,9 @@ def lib():
         L.moe_experts.restype = I
         L.moe_experts.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_experts_gate_up.restype = I
-        L.moe_experts_gate_up.argtypes = [D, P, P, P, P, P, P, P]
+        L.moe_experts_gate_up.argtypes = [D, P, P, P, P, P, P, P, S, P]
         L.moe_experts_down.restype = I
-        L.moe_experts_down.argtypes = [D, P, P, P, P, P]
+        L.moe_experts_down.argtypes = [D, P, P, P, P, P, S, P]
         L.moe_combine.restype = I
         L.moe_combine.argtypes = [D, P, P, P, P, P]
         _lib = L
@@ -246,8 +246,9 @@ def experts(x, perm_src, offsets, W_gate, W_up, W_down, k, n_experts, want_h=Fal
     return Yp, H
 
 
-def experts_gate_up(x, perm_src, offsets, W_gate, W_up, k, n_experts, H=None):
-    """Gate/up grouped GEMM with the fused SiLU*mul epilogue.  Returns H."""
+def experts_gate_up(x, perm_src, offsets, W_gate, W_up, k, n_experts, H=None, workspace=None):
+    """Gate/up grouped GEMM with the fused SiLU*mul epilogue.  Returns H.  With a
+    workspace (alloc_workspace of the same description) tiles are balanced dynamically."""
     dev = x.device
     T, d = x.shape
     G, F, _ = W_gate.shape
@@ -256,14 +257,15 @@ def experts_gate_up(x, perm_src, offsets, W_gate, W_up, k, n_experts, H=None):
     if H is None:
         H = torch.empty(rows, F, dtype=x.dtype, device=dev)
     _require(H, "H", dev, x.dtype, (rows, F))
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     st = lib().moe_experts_gate_up(ctypes.byref(desc), _ptr(x), _ptr(perm_src), _ptr(offsets),
-                                   _ptr(W_gate), _ptr(W_up), _ptr(H), _stream(dev))
+                                   _ptr(W_gate), _ptr(W_up), _ptr(H), ws, wsb, _stream(dev))
     _check("moe_experts_gate_up", st)
     return H
 
 
-def experts_down(H, offsets, W_down, T, k, n_experts, Yp=None):
-    """Down grouped GEMM.  Returns Yp (float32)."""
+def experts_down(H, offsets, W_down, T, k, n_experts, Yp=None, workspace=None):
+    """Down grouped GEMM.  Returns Yp (float32).  Workspace as for experts_gate_up."""
     dev = H.device
     G, d, F = W_down.shape
     desc = make_desc(T, d, n_experts, F, k, G - n_experts, 0.0, H.dtype)
@@ -271,8 +273,9 @@ def experts_down(H, offsets, W_down, T, k, n_experts, Yp=None):
     if Yp is None:
         Yp = torch.empty(rows, d, dtype=torch.float32, device=dev)
     _require(Yp, "Yp", dev, torch.float32, (rows, d))
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     st = lib().moe_experts_down(ctypes.byref(desc), _ptr(H), _ptr(offsets), _ptr(W_down),
-                                _ptr(Yp), _stream(dev))
+                                _ptr(Yp), ws, wsb, _stream(dev))
     _check("moe_experts_down", st)
     return Yp
 

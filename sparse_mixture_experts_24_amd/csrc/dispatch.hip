@@ -54,10 +54,12 @@ hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t
 __global__ __launch_bounds__(256) void expert_scan_kernel(int32_t* __restrict__ blk, int64_t nb,
                                                           int E, const float* __restrict__ p_part,
                                                           int64_t T, int k, int32_t* __restrict__ counts,
-                                                          float* __restrict__ f, float* __restrict__ p) {
+                                                          float* __restrict__ f, float* __restrict__ p,
+                                                          int32_t* __restrict__ zero, int nzero) {
   __shared__ int wsum[4];
   __shared__ float red[256];
   const int e = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (e == 0 && t < nzero) zero[t] = 0;   // the grouped GEMMs' work counters, if asked
   int run = 0;
   for (int64_t b0 = 0; b0 < nb; b0 += 256) {
     const int64_t b = b0 + t;
@@ -93,9 +95,10 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(int32_t* __restrict__ 
 }
 
 hipError_t launch_expert_scan(int32_t* blk, int64_t nb, int E, const float* p_part, int64_t T,
-                              int k, int32_t* counts, float* f, float* p, hipStream_t s) {
+                              int k, int32_t* counts, float* f, float* p, int32_t* zero,
+                              int nzero, hipStream_t s) {
   hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(256), 0, s, blk, nb, E, p_part, T, k,
-                     counts, f, p);
+                     counts, f, p, zero, zero ? nzero : 0);
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ struct GemmArgs {
   int narrow_small;       // down GEMM: 128-column tiles for small groups (few tiles overall)
   int ksplit;             // 1, or 2: the K range in two halves, partial sums to out / out2
   void* out2;             // second partial output (ksplit == 2)
+  int* ctr;               // NULL, or 8 per-XCD unit counters, zero at launch
 };
 
 // Geometry of group g.
@@ -114,9 +115,9 @@ __device__ inline float silu_fast(float z) {
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 // Output tile BM x BN, BN = 256 (gate/up: 128 gate + the matching 128 up columns).
-// BM = 32*MB rows: 256 for groups of at least SMALL_GROUP_ROWS rows, 64 below that, so
-// small experts (decode, the tail of skewed or capacity-limited routing) do not pay for
-// 256-row MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate
+// BM = 32*MB rows: 256 for groups of at least SMALL_GROUP_ROWS rows (the last tile of a
+// group 64, 128 or 256, to fit the remainder), 64 below that, so small experts (decode,
+// the tail of skewed or capacity-limited routing) do not pay for 256-row MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate
 // + 32 up) and all BM A rows: MB x 2 blocks of 32x32 accumulators.
 //   * B (the weights) goes straight from global memory into MFMA operand registers,
 //     three register sets deep: the set for K-step t+2 is issued at step t, so a weight
@@ -138,6 +139,14 @@ constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 // whole launch short of tiles (decode-sized batches, where the GEMM streams weights and
 // every CU must take part).
 __device__ inline bool small_group(int M) { return M < SMALL_GROUP_ROWS; }
+// Rows of m-tile mt (tiles start at mt * 256 in large groups, mt * 64 in small ones):
+// large groups take 256-row tiles and put their remainder in one tile of 64, 128 or 256
+// rows, whichever is the smallest that holds it.
+__device__ inline int m_tile_rows(int M, int mt) {
+  if (small_group(M)) return BM_SMALL;
+  const int r = M - mt * BM_BIG;
+  return r >= BM_BIG ? BM_BIG : (r <= 64 ? 64 : (r <= 128 ? 128 : BM_BIG));
+}
 template <bool GATED>
 __device__ inline int tile_cols(bool small, int narrow_small) {
   return GATED ? 128 : ((small && narrow_small) ? 128 : 256);
@@ -323,10 +332,55 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
   }
 }
 
+// One work unit: (K half, tile) of the table built in LDS.
+template <bool GATED>
+__device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
+                                               const int* tiles, int64_t ntile, int64_t unit) {
+  const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
+  const int ks = (int)(unit / ntile);
+  const int64_t tile = unit - ks * ntile;
+  const int k0 = ks * nk_half, nk = min(nk_half, nk_all - k0);
+  void* outp = ks == 0 ? a.out : a.out2;
+  const int g = find_group(tiles, a.G, tile);
+  int64_t row_begin;
+  int M;
+  group_rows(a, g, row_begin, M);
+  const bool sm = small_group(M);
+  const int narrow = a.narrow_small;
+  const int mt_g = (M + (sm ? BM_SMALL : BM_BIG) - 1) / (sm ? BM_SMALL : BM_BIG);
+  const int local = (int)(tile - tiles[g]);          // ordered (n-tile, m-tile)
+  const int mt = local % mt_g;
+  const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
+  const int rows = m_tile_rows(M, mt);
+  if (!sm && rows == BM_BIG)
+    gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
+                                          outp);
+  else if (!sm && rows == 128)
+    gemm_bf16_tile<128 / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
+                                       outp);
+  else if (!sm)
+    gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
+                                            nk, outp);
+  else if (GATED || !narrow)
+    gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0, k0,
+                                            nk, outp);
+  else if constexpr (!GATED)
+    gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0, k0,
+                                            nk, outp);
+}
+
+// Persistent kernel over the work units, in table order (group, n-tile, m-tile), split
+// into 8 contiguous ranges, one per XCD (blocks are dispatched to XCDs round-robin), so
+// the m-tiles that share a weight tile run on the same L2.  With counters (a.ctr, 8 ints,
+// zero at launch) each block takes its XCD's next unit and, once that range is done,
+// the other ranges' in turn: blocks that drew cheap tiles (a group's 64- or 128-row
+// remainder) take more.  Without counters each block takes every gridDim.x-th unit of
+// its range.
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
+  __shared__ long long next_unit;
   const int N = a.N, narrow = a.narrow_small;
   auto tile_count = [N, narrow](int M) {
     const bool sm = small_group(M);
@@ -336,32 +390,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   build_tile_table(a, tile_count, tiles);   // ends with a barrier
   const int64_t ntile = tiles[a.G];
   const int64_t total = ntile * a.ksplit;    // work units: (K half, tile)
-  const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
-  const int per = gridDim.x >> 3;
-  const int64_t first = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  for (int64_t unit = first; unit < total; unit += gridDim.x) {
-    const int ks = (int)(unit / ntile);
-    const int64_t tile = unit - ks * ntile;
-    const int k0 = ks * nk_half, nk = min(nk_half, nk_all - k0);
-    void* outp = ks == 0 ? a.out : a.out2;
-    const int g = find_group(tiles, a.G, tile);
-    int64_t row_begin;
-    int M;
-    group_rows(a, g, row_begin, M);
-    const bool sm = small_group(M);
-    const int mt_g = (M + (sm ? BM_SMALL : BM_BIG) - 1) / (sm ? BM_SMALL : BM_BIG);
-    const int local = (int)(tile - tiles[g]);          // ordered (n-tile, m-tile)
-    const int mt = local % mt_g;
-    const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
-    if (!sm)
-      gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
-                                            nk, outp);
-    else if (GATED || !narrow)
-      gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                              k0, nk, outp);
-    else if constexpr (!GATED)
-      gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                              k0, nk, outp);
+  const int x = blockIdx.x & 7;
+  if (a.ctr == nullptr) {
+    const int per = gridDim.x >> 3;
+    for (int64_t unit = (int64_t)x * per + (blockIdx.x >> 3); unit < total; unit += gridDim.x)
+      gemm_bf16_unit<GATED>(a, smem, tiles, ntile, unit);
+    return;
+  }
+  const int64_t per_x = (total + 7) / 8;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      long long u = -1;
+      for (int r = 0; r < 8 && u < 0; ++r) {
+        const int xr = (x + r) & 7;
+        const int64_t lo = xr * per_x, hi = min(total, lo + per_x);
+        if (lo >= hi) continue;
+        const int c = atomicAdd(&a.ctr[xr], 1);
+        if (lo + c < hi) u = lo + c;
+      }
+      next_unit = u;
+    }
+    __syncthreads();
+    const int64_t unit = next_unit;
+    __syncthreads();   // read by all before thread 0 writes the next one
+    if (unit < 0) break;
+    gemm_bf16_unit<GATED>(a, smem, tiles, ntile, unit);
   }
 }
 
@@ -439,6 +492,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   }
 }
 
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, s, p, n);
+  return hipGetLastError();
+}
+
 static int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -484,6 +547,13 @@ static GemmArgs base_args(const moe_desc_t& d, const int32_t* offsets) {
   return a;
 }
 
+// Dynamic tile order pays off where tile costs differ (large groups with 64-, 128- or
+// 256-row remainder tiles); for decode-sized batches (all groups small, every tile alike)
+// the counter round trip per tile is pure cost.
+static bool dynamic_tiles(const moe_desc_t& d) {
+  return d.T * d.top_k >= (int64_t)SMALL_GROUP_ROWS * d.n_experts;
+}
+
 // Upper bound of sum_g ceil(M_g / bm): ceil(T*k / bm) + E (+ ceil(T / bm) shared).
 static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
   return ceil_div(d.T * d.top_k, bm) + d.n_experts + (d.n_shared ? ceil_div(d.T, bm) : 0);
@@ -491,7 +561,7 @@ static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
 
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
                           const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s) {
+                          int32_t* ctr, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, offsets);
   a.A = x;
@@ -503,6 +573,7 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
   a.ksplit = 1;
+  a.ctr = dynamic_tiles(d) ? ctr : nullptr;
   return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128), s)
             : run_f32<true>(a, max_m_tiles(d, 64), s);
 }
@@ -524,7 +595,7 @@ bool down_split_k(const moe_desc_t& d) {
 }
 
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, float* Yp2, hipStream_t s) {
+                       const void* W_down, float* Yp, float* Yp2, int32_t* ctr, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, offsets);
   a.A = H;
@@ -541,6 +612,7 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
   }
   a.ksplit = (bf && Yp2) ? 2 : 1;
   a.out2 = Yp2;
+  a.ctr = dynamic_tiles(d) ? ctr : nullptr;
   return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128), s)
             : run_f32<false>(a, max_m_tiles(d, 64), s);
 }

@@ -51,6 +51,7 @@ Workspace carve_workspace(const moe_desc_t& d, void* base) {
   w.p_part = (float*)take(rp.n_blocks * E * 4);
   w.cnt_part = (int32_t*)take(nbh * E * 4);
   w.counts = (int32_t*)take(E * 4);
+  w.ctr = (int32_t*)take(kTileCounters * 4);
   w.offsets = (int32_t*)take((E + 1) * 4);
   w.perm_src = (int32_t*)take(TK * 4);
   w.slot_pos = (int32_t*)take(TK * 4);
@@ -131,7 +132,7 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, w.p_part, w.cnt_part, s));
   if (f || p)
     MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
-                               (int)d.top_k, w.counts, f, p, s));
+                               (int)d.top_k, w.counts, f, p, nullptr, 0, s));
   return MOE_OK;
 }
 
@@ -151,7 +152,7 @@ moe_status_t moe_dispatch(const moe_desc_t* desc, const int32_t* topk_idx, int32
   const int64_t C = capacity_of(d);
   MOE_HIP(launch_hist(topk_idx, TK, E, kDispatchChunk, w.cnt_part, s));
   MOE_HIP(launch_expert_scan(w.cnt_part, ceil_div(TK, kDispatchChunk), E, nullptr, d.T,
-                             (int)d.top_k, counts, nullptr, nullptr, s));
+                             (int)d.top_k, counts, nullptr, nullptr, nullptr, 0, s));
   MOE_HIP(launch_scatter(topk_idx, TK, E, kDispatchChunk, C, w.cnt_part, counts, offsets,
                          perm_src, slot_pos, s));
   return MOE_OK;
@@ -174,31 +175,51 @@ moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* p
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   void* h = H ? H : w.H;
-  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, W_gate, W_up, h, s));
-  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, nullptr, s));
+  MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
+  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, W_gate, W_up, h, w.ctr, s));
+  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, nullptr, w.ctr + 8, s));
   return MOE_OK;
+}
+
+// Work counters of an optional workspace (NULL: static tile order).
+static moe_status_t optional_ctr(const moe_desc_t& d, void* ws, size_t bytes, int32_t** ctr) {
+  *ctr = nullptr;
+  if (!ws) return MOE_OK;
+  Workspace w;
+  const moe_status_t st = check_ws(d, ws, bytes, w);
+  if (st == MOE_OK) *ctr = w.ctr;
+  return st;
 }
 
 moe_status_t moe_experts_gate_up(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
                                  const int32_t* offsets, const void* W_gate, const void* W_up,
-                                 void* H, void* stream) {
+                                 void* H, void* workspace, size_t workspace_bytes, void* stream) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   if (!offsets || !W_gate || !W_up || (desc->T > 0 && (!x || !perm_src || !H)))
     return MOE_E_NULL;
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(H))
     return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, W_gate, W_up, H, (hipStream_t)stream));
+  int32_t* ctr;
+  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctr) MOE_HIP(launch_zero_i32(ctr, 8, s));
+  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, W_gate, W_up, H, ctr, s));
   return MOE_OK;
 }
 
 moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32_t* offsets,
-                              const void* W_down, float* Yp, void* stream) {
+                              const void* W_down, float* Yp, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   if (!offsets || !W_down || (desc->T > 0 && (!H || !Yp))) return MOE_E_NULL;
   if (!aligned16(H) || !aligned16(W_down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, nullptr, (hipStream_t)stream));
+  int32_t* ctr;
+  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
+  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, nullptr, ctr ? ctr + 8 : nullptr, s));
   return MOE_OK;
 }
 
@@ -234,11 +255,11 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
   MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, w.p_part, w.cnt_part, s));
   MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
-                             f, p, s));
+                             f, p, w.ctr, kTileCounters, s));
   MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
                          w.perm_src, w.slot_pos, s));
-  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, s));
-  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, w.Yp2, s));
+  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, w.ctr, s));
+  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, w.Yp2, w.ctr + 8, s));
   MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
   return MOE_OK;
 }

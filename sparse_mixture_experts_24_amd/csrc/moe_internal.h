@@ -47,6 +47,7 @@ struct Workspace {
   int32_t* slot_pos;   // [T*k]
   void* H;             // [T*k + S*T, F] dtype
   float* Yp;           // [T*k + S*T, d]
+  int32_t* ctr;        // kTileCounters work counters of the grouped GEMMs
   float* Yp2;          // second partial of the split down GEMM, or NULL
   size_t bytes;        // minimum size (without Yp2)
   size_t bytes_full;   // with Yp2 when the layer splits its down GEMM
@@ -61,17 +62,23 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
                         int32_t* cnt_part, hipStream_t s);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
+// zero (optional): nzero <= 256 int32 that block 0 also sets to zero.
 hipError_t launch_expert_scan(int32_t* blk, int64_t nb, int E, const float* p_part, int64_t T,
-                              int k, int32_t* counts, float* f, float* p, hipStream_t s);
+                              int k, int32_t* counts, float* f, float* p, int32_t* zero,
+                              int nzero, hipStream_t s);
 hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int64_t C,
                           const int32_t* blk_base, const int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
                           const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s);
+                          int32_t* ctr, hipStream_t s);
 // Yp2 non-NULL (bf16 layers): K split in two, partial sums in Yp and Yp2.
+// ctr: NULL (static tile order) or 8 int32 work counters, zero at launch.
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, float* Yp2, hipStream_t s);
+                       const void* W_down, float* Yp, float* Yp2, int32_t* ctr, hipStream_t s);
+// Sets n int32 to zero (a kernel, so that it may sit in a captured graph).
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+constexpr int kTileCounters = 16;   // 8 per grouped GEMM
 bool down_split_k(const moe_desc_t& d);
 // Yp2 non-NULL: the per-slot outputs are Yp + Yp2.
 hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,

@@ -122,9 +122,15 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need // 4, None) == 4
     assert L.moe_forward(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, None, None, P(0x100010), ws_need, None) == 4
     assert L.moe_dispatch(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 0, None) == 4
+    # the stage GEMMs take an optional workspace: given, it must be large enough and aligned
+    assert L.moe_experts_gate_up(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 256, None) == 4
+    assert L.moe_experts_gate_up(ctypes.byref(d), fake, fake, fake, fake, fake, fake, P(0x100010), ws_need, None) == 4
+    assert L.moe_experts_down(ctypes.byref(d), fake, fake, fake, fake, fake, 256, None) == 4
+    assert L.moe_experts_down(ctypes.byref(d), None, fake, fake, fake, None, 0, None) == 1
     # misaligned tensors
     odd = P(0x100004)
     assert L.moe_forward(ctypes.byref(d), odd, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 3
+    assert L.moe_experts_gate_up(ctypes.byref(d), odd, fake, fake, fake, fake, fake, None, 0, None) == 3
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):
