@@ -24,7 +24,10 @@ __device__ inline void store4<bf16_t>(bf16_t* out, int64_t i, float4 v) {
 }
 
 // Yp2 (optional): second partial of a K-split down GEMM; a slot's output is Yp + Yp2.
-template <typename OutT>
+// The slots are read KB at a time, all loads of a batch issued before any is used (a
+// dropped slot loads row 0 and contributes nothing), so each thread keeps KB (or 2 KB)
+// 16-byte loads in flight; the sum runs over the slots in ascending order.
+template <typename OutT, int KB, bool SPLIT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp,
                                                       const float* __restrict__ Yp2,
                                                       const int32_t* __restrict__ slot_pos,
@@ -41,26 +44,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t srow = (int64_t)T * k + t;
   for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int pos = sp[j];
-      if (pos < 0) continue;
-      float4 v = *reinterpret_cast<const float4*>(Yp + (int64_t)pos * d + c);
-      if (Yp2) {
-        const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + (int64_t)pos * d + c);
-        v.x += v2.x;
-        v.y += v2.y;
-        v.z += v2.z;
-        v.w += v2.w;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      float4 v[KB];
+      bool ok[KB];
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        const int j = j0 + q;
+        const int pos = j < k ? sp[j] : -1;
+        ok[q] = pos >= 0;
+        const int64_t off = (int64_t)(ok[q] ? pos : 0) * d + c;
+        v[q] = *reinterpret_cast<const float4*>(Yp + off);
+        if constexpr (SPLIT) {
+          const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + off);
+          v[q].x += v2.x;
+          v[q].y += v2.y;
+          v[q].z += v2.z;
+          v[q].w += v2.w;
+        }
       }
-      const float wj = sw[j];
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        if (!ok[q]) continue;
+        const float wj = sw[j0 + q];
+        acc.x = fmaf(wj, v[q].x, acc.x);
+        acc.y = fmaf(wj, v[q].y, acc.y);
+        acc.z = fmaf(wj, v[q].z, acc.z);
+        acc.w = fmaf(wj, v[q].w, acc.w);
+      }
     }
     if (shared) {
       float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
-      if (Yp2) {
+      if constexpr (SPLIT) {
         const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + srow * d + c);
         v.x += v2.x;
         v.y += v2.y;
@@ -76,17 +90,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+template <typename OutT, bool SPLIT>
+static void launch_combine_t(const moe_desc_t& d, const float* Yp, const float* Yp2,
+                             const int32_t* slot_pos, const float* topk_w, OutT* out,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)d.T), block(256);
+  const int T = (int)d.T, k = (int)d.top_k, dm = (int)d.d_model, sh = (int)d.n_shared;
+  if (k == 1)
+    hipLaunchKernelGGL((combine_kernel<OutT, 1, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
+                       topk_w, T, k, dm, sh, out);
+  else if (k == 2)
+    hipLaunchKernelGGL((combine_kernel<OutT, 2, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
+                       topk_w, T, k, dm, sh, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<OutT, 4, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
+                       topk_w, T, k, dm, sh, out);
+}
+
+template <typename OutT>
+static void launch_combine_o(const moe_desc_t& d, const float* Yp, const float* Yp2,
+                             const int32_t* slot_pos, const float* topk_w, OutT* out,
+                             hipStream_t s) {
+  if (Yp2)
+    launch_combine_t<OutT, true>(d, Yp, Yp2, slot_pos, topk_w, out, s);
+  else
+    launch_combine_t<OutT, false>(d, Yp, Yp2, slot_pos, topk_w, out, s);
+}
+
 hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
                           const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  const dim3 grid((unsigned)d.T), block(256);
-  const int T = (int)d.T, k = (int)d.top_k, dm = (int)d.d_model, sh = (int)d.n_shared;
   if (d.out_dtype == MOE_DTYPE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, Yp, Yp2, slot_pos, topk_w, T, k, dm,
-                       sh, (float*)out);
+    launch_combine_o<float>(d, Yp, Yp2, slot_pos, topk_w, (float*)out, s);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s, Yp, Yp2, slot_pos, topk_w, T, k, dm,
-                       sh, (bf16_t*)out);
+    launch_combine_o<bf16_t>(d, Yp, Yp2, slot_pos, topk_w, (bf16_t*)out, s);
   return hipGetLastError();
 }
 
