@@ -369,13 +369,13 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
                                             nk, outp);
 }
 
-// Persistent kernel over the work units, in table order (group, n-tile, m-tile), split
-// into 8 contiguous ranges, one per XCD (blocks are dispatched to XCDs round-robin), so
-// the m-tiles that share a weight tile run on the same L2.  With counters (a.ctr, 8 ints,
-// zero at launch) each block takes its XCD's next unit and, once that range is done,
-// the other ranges' in turn: blocks that drew cheap tiles (a group's 64- or 128-row
-// remainder) take more.  Without counters each block takes every gridDim.x-th unit of
-// its range.
+// Persistent kernel over the work units in table order (group, n-tile, m-tile), dealt to
+// the 8 XCDs (blocks are dispatched to XCDs round-robin) in windows of 32 consecutive
+// units, so that the m-tiles sharing a weight tile run at the same time on one L2.
+// Without counters block b takes unit 32 (8 r + b % 8) + b / 8 of round r (grid of 256).
+// With counters (a.ctr, 8 ints, zero at launch) each block takes its XCD's next unit
+// when it is free, so blocks that drew cheap tiles (a group's 64- or 128-row remainder)
+// take more, and an XCD that runs out helps the others.
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
@@ -397,16 +397,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       gemm_bf16_unit<GATED>(a, smem, tiles, ntile, unit);
     return;
   }
-  const int64_t per_x = (total + 7) / 8;
   for (;;) {
     if (threadIdx.x == 0) {
+      // XCD xr's c-th unit: the units are dealt out to the XCDs in windows of W
+      // consecutive ones, round-robin (the static order's windows); an XCD whose windows
+      // are used up takes the next XCD's in turn.
+      constexpr int W = 32;
       long long u = -1;
       for (int r = 0; r < 8 && u < 0; ++r) {
         const int xr = (x + r) & 7;
-        const int64_t lo = xr * per_x, hi = min(total, lo + per_x);
-        if (lo >= hi) continue;
         const int c = atomicAdd(&a.ctr[xr], 1);
-        if (lo + c < hi) u = lo + c;
+        const int64_t cand = ((int64_t)(c / W) * 8 + xr) * W + c % W;
+        if (cand < total) u = cand;
       }
       next_unit = u;
     }
