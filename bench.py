@@ -310,7 +310,7 @@ def cpu_baseline(wl, inp, sample):
         cores = os.cpu_count()
     if not sample:
         per_tok = 6.0 * wl.d * wl.F * (wl.k + wl.n_shared)
-        sample = int(max(8, min(wl.T, 1.0e12 / per_tok)))
+        sample = int(max(8, min(wl.T, 6.0e12 / per_tok)))   # ~10-20 s of oracle work
     t0 = time.perf_counter()
     x = mo._np(inp["x"])
     r = oracle.route(x, mo._np(inp["W_router"]), wl.k, mo._np(inp["router_bias"]))
