@@ -152,6 +152,194 @@ __device__ inline int tile_cols(bool small, int narrow_small) {
   return GATED ? 128 : ((small && narrow_small) ? 128 : 256);
 }
 
+// Epilogue of a tile: D[m][n] of a 32x32 block sits in lane n + 32*((m/4)%2), register
+// 4*(m/8) + m%4.  Gate/up: h = SiLU(g) * u -> bf16 into an LDS tile [BM][128 + 8] (the A
+// stages are free: every block barrier of the K loop is behind), then 16-byte row stores.
+// Down: fp32 stores of the lanes' columns.
+template <int MB, int NB, bool GATED>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[MB][NB], bf16_t* smem,
+                                           void* outp, int64_t row_begin, int M, int m0,
+                                           int ncol0, int N, const int (&bcol)[NB]) {
+  constexpr int BMT = 32 * MB;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fr = lane & 31, fg = lane >> 5;
+  if (GATED) {
+    constexpr int HLD = 136;
+    bf16_t* Ht = smem;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
+        Ht[row * HLD + 32 * w + fr] =
+            f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][NB - 1][r]);
+      }
+    __syncthreads();
+    bf16_t* H = (bf16_t*)outp;
+#pragma unroll 4
+    for (int i = 0; i < BMT / 16; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, cc = (c & 15) * 8;
+      const int m = m0 + row, n = ncol0 + cc;   // N % 64 == 0: n < N implies n + 8 <= N
+      if (m < M && n < N)
+        *reinterpret_cast<u32x4*>(H + (row_begin + m) * N + n) =
+            *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
+    }
+    __syncthreads();   // the next tile's prologue overwrites the LDS
+  } else {
+    float* Y = (float*)outp;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = bcol[nb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
+          if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
+        }
+      }
+  }
+}
+
+// A 64-row tile whose work is streaming its weights (small groups: decode, the tail of
+// skewed or capacity-limited routing).  Same math as gemm_bf16_tile<2, NB, GATED>, but the
+// weights are read with whole 128-byte row segments per 8 lanes (HBM-friendly, where the
+// register-direct layout has 32 rows x 32 bytes per load) and put into MFMA order through
+// a wave-private LDS buffer: two stages of [NB*32 rows][64 bf16], 16-byte chunks XOR
+// swizzled (chunk c of row r at c ^ ((r/2)%8)) so both the stores and the fragment reads
+// are conflict-free.  P steps of weights are in flight per wave (P register sets).
+constexpr int SB_STAGE = 2 * 32 * BK;                 // bf16 per wave stage, NB <= 2
+constexpr size_t SMALL_LDS_BYTES =
+    (size_t)(2 * 64 * LDK + 4 * 2 * SB_STAGE) * sizeof(bf16_t);   // A stages + B buffers
+// Steps of weights in flight per wave (measured on decode-sized launches: about 16 KB
+// (two-block tiles) to 32 KB (one-block down tiles) per wave is best; more is slower).
+constexpr int STREAM_P2 = 2, STREAM_P1 = 8;
+constexpr size_t KERNEL_LDS_BYTES =
+    GEMM_LDS_BYTES > SMALL_LDS_BYTES ? GEMM_LDS_BYTES : SMALL_LDS_BYTES;
+template <int NB, bool GATED, int P>
+__device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t* smem, int g,
+                                                      int64_t row_begin, int M, int m0,
+                                                      int ncol0, int k0, int nk, void* outp) {
+  static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
+  static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
+  constexpr int MB = 2, BMT = 64, STAGE = BMT * LDK, NL = 4 * NB;   // NL: B loads per step
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const int fr = lane & 31, fg = lane >> 5;
+  const bf16_t* A = (const bf16_t*)a.A + k0 * BK;
+  const int K = a.K, N = a.N;
+  bf16_t* Bw = smem + 2 * STAGE + w * 2 * SB_STAGE;   // this wave's two B stages
+
+  int aoff[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + lr + 32 * i;
+    aoff[i] = m < M ? m : 0;
+  }
+  if (GATED && g < a.E) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = a.perm_src[row_begin + aoff[i]];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = aoff[i] / a.topk * K + lc;
+  } else {
+    const int base = GATED ? 0 : (int)row_begin;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aoff[i] = (base + aoff[i]) * K + lc;
+  }
+  // B load j (j < NL): block nb = j / 4, rows r = 8 (j % 4) + lane / 8 of the block, the
+  // lane's 16-byte chunk c = lane % 8; stored at chunk position c ^ ((r / 2) % 8).
+  const bf16_t* pbl[NL];
+  int bst[NL];
+  int bcol[NB];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int nb = j / 4, r = 8 * (j % 4) + (lane >> 3), c = lane & 7;
+    const int n = GATED ? ncol0 + 32 * w + r : ncol0 + 32 * NB * w + 32 * nb + r;
+    const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
+    pbl[j] = base + ((int64_t)g * N + min(n, N - 1)) * K + 8 * c + k0 * BK;
+    bst[j] = (nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    bcol[nb] = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
+  int brd[4];   // fragment read offsets: row fr of a block, chunk 4 fg + s
+#pragma unroll
+  for (int s = 0; s < 4; ++s) brd[s] = fr * BK + 8 * ((4 * fg + s) ^ ((fr >> 1) & 7));
+
+  floatx16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4 rb[P][NL];   // weights of steps in flight: set q holds step t with t % P == q
+  u32x4 ra[MB];
+
+#define MOE_SLOAD_B(q, t)                                                                  \
+  _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
+    rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + min((t), nk - 1) * BK);
+#define MOE_SSTORE_B(q, st)                                                                \
+  _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
+    *reinterpret_cast<u32x4*>(Bw + (st) * SB_STAGE + bst[j]) = rb[q][j];
+#define MOE_SLOAD_A(t)                                                                     \
+  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
+    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (t) * BK);
+#define MOE_SSTORE_A(st)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
+    *reinterpret_cast<u32x4*>(smem + (st) * STAGE + (lr + 32 * i) * LDK + lc) = ra[i];
+  // K step t: the weights of step t+1 go from their register set into this wave's LDS
+  // stage (t+1)%2 and the set is refilled with step t+1+P; the MFMAs of step t read the
+  // stages t%2; the token rows of step t+1 are stored; block barrier.  Steps t >= nk
+  // (padding to a multiple of P) see zero token rows.
+#define MOE_SSTEP(t, q1)                                                                   \
+  {                                                                                        \
+    MOE_SLOAD_A(min((t) + 1, nk - 1));                                                     \
+    MOE_SSTORE_B(q1, ((t) + 1) & 1);                                                       \
+    MOE_SLOAD_B(q1, (t) + 1 + P);                                                          \
+    const bf16_t* As_ = smem + ((t) & 1) * STAGE;                                          \
+    const bf16_t* Bs_ = Bw + ((t) & 1) * SB_STAGE;                                         \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                        \
+      bf16x8 af[MB], bfr[NB];                                                              \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
+        af[mb] = *reinterpret_cast<const bf16x8*>(As_ + (mb * 32 + fr) * LDK + 32 * fg + 8 * s); \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                    \
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs_ + nb * 32 * BK + brd[s]);          \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
+        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                  \
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], \
+                                                                0, 0, 0);                  \
+    }                                                                                      \
+    if ((t) + 1 >= nk) {                                                                   \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) ra[i] = u32x4{0u, 0u, 0u, 0u};        \
+    }                                                                                      \
+    MOE_SSTORE_A(((t) + 1) & 1);                                                           \
+    __syncthreads();                                                                       \
+  }
+
+  // Prologue: weights of steps 0..P-1 requested, step 0's stored; token rows of step 0.
+#pragma unroll
+  for (int q = 0; q < P; ++q) MOE_SLOAD_B(q, q);
+  MOE_SSTORE_B(0, 0);
+  MOE_SLOAD_B(0, P);
+  MOE_SLOAD_A(0);
+  MOE_SSTORE_A(0);
+  __syncthreads();
+  const int nkp = (nk + P - 1) / P * P;
+  for (int kt = 0; kt < nkp; kt += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) MOE_SSTEP(kt + u, (u + 1) % P);   // (u: the macros use j)
+  }
+#undef MOE_SLOAD_B
+#undef MOE_SSTORE_B
+#undef MOE_SLOAD_A
+#undef MOE_SSTORE_A
+#undef MOE_SSTEP
+  store_tile<MB, NB, GATED>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol);
+}
+
 // One output tile over K steps [k0, k0 + nk) (the whole K unless split), into outp.
 template <int MB, int NB, bool GATED>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
@@ -291,45 +479,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #undef MOE_INTERLEAVE
 #undef MOE_STEP
 
-  // Epilogue.  D[m][n] of a 32x32 block: lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
-  if (GATED) {
-    // h = SiLU(g) * u -> bf16 into an LDS tile [BM][128 + 8], then 16-byte row stores.
-    // (The A stages are free: the last K step ended with a barrier.)
-    constexpr int HLD = 136;
-    bf16_t* Ht = smem;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
-        Ht[row * HLD + 32 * w + fr] = f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][1][r]);
-      }
-    __syncthreads();
-    bf16_t* H = (bf16_t*)outp;
-#pragma unroll 4
-    for (int i = 0; i < BMT / 16; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, cc = (c & 15) * 8;
-      const int m = m0 + row, n = ncol0 + cc;   // N % 64 == 0: n < N implies n + 8 <= N
-      if (m < M && n < N)
-        *reinterpret_cast<u32x4*>(H + (row_begin + m) * N + n) =
-            *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
-    }
-    __syncthreads();   // the next tile's prologue overwrites the LDS
-  } else {
-    float* Y = (float*)outp;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int n = bcol[nb];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
-          if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
-        }
-      }
-  }
+  store_tile<MB, NB, GATED>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol);
 }
 
 // One work unit: (K half, tile) of the table built in LDS.
@@ -362,11 +512,11 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
     gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
                                             nk, outp);
   else if (GATED || !narrow)
-    gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0, k0,
-                                            nk, outp);
+    gemm_bf16_tile_stream<2, GATED, STREAM_P2>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+                                               k0, nk, outp);
   else if constexpr (!GATED)
-    gemm_bf16_tile<BM_SMALL / 32, 1, GATED>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0, k0,
-                                            nk, outp);
+    gemm_bf16_tile_stream<1, GATED, STREAM_P1>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+                                               k0, nk, outp);
 }
 
 // Persistent kernel over the work units in table order (group, n-tile, m-tile), dealt to
@@ -518,7 +668,7 @@ static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) 
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)GEMM_LDS_BYTES);
+                                       (int)KERNEL_LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -526,7 +676,8 @@ static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) 
   if (max_tiles < grid) grid = max_tiles;
   grid = round_up(grid, 8);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_bf16_kernel<GATED>, dim3((unsigned)grid), dim3(256), GEMM_LDS_BYTES, s, a);
+  hipLaunchKernelGGL(gemm_bf16_kernel<GATED>, dim3((unsigned)grid), dim3(256), KERNEL_LDS_BYTES,
+                     s, a);
   return hipGetLastError();
 }
 
