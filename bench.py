@@ -121,7 +121,7 @@ def main():
     out2 = torch.empty_like(out)
     calls = [
         ("route", lambda: L.moe_route(dref, P(dinp["x"]), P(dinp["W_router"]),
-                                      P(dinp["router_bias"]), P(idx), P(w), P(f), P(p), P(ws),
+                                      P(dinp["router_bias"]), P(idx), P(w), None, P(f), P(p), P(ws),
                                       ws.numel(), sp)),
         ("dispatch", lambda: L.moe_dispatch(dref, P(idx), P(counts), P(offsets), P(perm),
                                             P(slot), P(ws), ws.numel(), sp)),

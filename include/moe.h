@@ -113,12 +113,14 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
  * ("Chapter 30", 30.2.3; "MoE memo", auxiliary-loss and DeepSeek-V3 sections.)
  *   topk_idx [T, k] int32   chosen experts, slot order = selection score descending
  *   topk_w   [T, k] float32 renormalised weights from the unbiased probabilities
+ *   gap      [T] float32 or NULL: s_(k) - s_(k+1), the k-th largest selection score minus
+ *            the (k+1)-th (+inf when k == E); how close the token is to routing otherwise
  *   f, p     [E] float32 or NULL
  * Errors: MOE_E_NULL (x, W_router, topk_idx, topk_w), MOE_E_SHAPE, MOE_E_UNSUPPORTED,
  * MOE_E_WORKSPACE, MOE_E_HIP. */
 moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_router,
                        const float* router_bias, int32_t* topk_idx, float* topk_w,
-                       float* f, float* p, void* workspace, size_t workspace_bytes,
+                       float* gap, float* f, float* p, void* workspace, size_t workspace_bytes,
                        void* stream);
 
 /* Expert histogram, capacity, prefix sum and the stable permutation.

@@ -69,7 +69,7 @@ def lib():
         L.moe_forward.restype = I
         L.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_route.restype = I
-        L.moe_route.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
+        L.moe_route.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_dispatch.restype = I
         L.moe_dispatch.argtypes = [D, P, P, P, P, P, P, S, P]
         L.moe_experts.restype = I
@@ -185,8 +185,10 @@ def forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor=0
     return out, f, p
 
 
-def route(x, W_router, router_bias, k, workspace=None, W_gate_shape=None, n_shared=0):
-    """Router + top-k + renorm + statistics.  Returns (topk_idx, topk_w, f, p)."""
+def route(x, W_router, router_bias, k, workspace=None, W_gate_shape=None, n_shared=0,
+          want_gap=False):
+    """Router + top-k + renorm + statistics.  Returns (topk_idx, topk_w, f, p), and the
+    per-token gap s_(k) - s_(k+1) as a fifth value when want_gap."""
     dev = x.device
     T, d = x.shape
     E = W_router.shape[0]
@@ -198,11 +200,13 @@ def route(x, W_router, router_bias, k, workspace=None, W_gate_shape=None, n_shar
     w = torch.empty(T, k, dtype=torch.float32, device=dev)
     f = torch.empty(E, dtype=torch.float32, device=dev)
     p = torch.empty(E, dtype=torch.float32, device=dev)
+    gap = torch.empty(T, dtype=torch.float32, device=dev) if want_gap else None
     ws = _ws(desc, dev, workspace)
     st = lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(router_bias),
-                         _ptr(idx), _ptr(w), _ptr(f), _ptr(p), _ptr(ws), ws.numel(), _stream(dev))
+                         _ptr(idx), _ptr(w), _ptr(gap), _ptr(f), _ptr(p), _ptr(ws), ws.numel(),
+                         _stream(dev))
     _check("moe_route", st)
-    return idx, w, f, p
+    return (idx, w, f, p, gap) if want_gap else (idx, w, f, p)
 
 
 def dispatch(topk_idx, n_experts, capacity_factor=0.0, workspace=None):

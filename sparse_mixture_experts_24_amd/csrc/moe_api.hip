@@ -117,8 +117,9 @@ int64_t moe_capacity(const moe_desc_t* desc) {
 }
 
 moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_router,
-                       const float* router_bias, int32_t* topk_idx, float* topk_w, float* f,
-                       float* p, void* workspace, size_t workspace_bytes, void* stream) {
+                       const float* router_bias, int32_t* topk_idx, float* topk_w, float* gap,
+                       float* f, float* p, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
@@ -129,7 +130,8 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const RoutePlan rp = route_plan(d);
-  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, w.p_part, w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, gap, w.p_part, w.cnt_part,
+                       s));
   if (f || p)
     MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
                                (int)d.top_k, w.counts, f, p, nullptr, 0, s));
@@ -253,7 +255,8 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
   const int E = (int)d.n_experts;
   const int64_t C = capacity_of(d);
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
-  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, w.p_part, w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, w.p_part,
+                       w.cnt_part, s));
   MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
                              f, p, w.ctr, kTileCounters, s));
   MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,

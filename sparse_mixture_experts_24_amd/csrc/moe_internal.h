@@ -57,9 +57,10 @@ Workspace carve_workspace(const moe_desc_t& d, void* base);
 constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe_dispatch
 
 // ---------------------------------------------------------------- launchers
+// gap (optional, [T]): s_(k) - s_(k+1) of each token's selection scores (+inf if k == E).
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
-                        const float* bias, int32_t* topk_idx, float* topk_w, float* p_part,
-                        int32_t* cnt_part, hipStream_t s);
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
+                        float* p_part, int32_t* cnt_part, hipStream_t s);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
 // zero (optional): nzero <= 256 int32 that block 0 also sets to zero.

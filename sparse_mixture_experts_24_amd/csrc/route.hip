@@ -37,7 +37,8 @@ __device__ inline float wave_sum(float v) {
 template <int E_PAD>
 __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E, int k,
                                   const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
-                                  float* __restrict__ topk_w, float* psum, int* cnt) {
+                                  float* __restrict__ topk_w, float* __restrict__ gap,
+                                  float* psum, int* cnt) {
   constexpr int NV = (E_PAD + 63) / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bv[NV];
@@ -78,8 +79,10 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
     }
     unsigned taken = 0;
     int my_idx = 0;
-    float my_p = 0.0f;
-    for (int r = 0; r < k; ++r) {
+    float my_p = 0.0f, s_k = 0.0f;
+    // k rounds of wavefront argmax (one more, not taken, when the gap is asked for)
+    const int rounds = k + (gap != nullptr ? 1 : 0);
+    for (int r = 0; r < rounds; ++r) {
       float bvv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
@@ -98,6 +101,11 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
           be = oe;
         }
       }
+      if (r == k) {            // gap = s_(k) - s_(k+1); +inf when k == E
+        if (lane == 0) gap[t] = s_k - bvv;
+        break;
+      }
+      s_k = bvv;
       const bool ok = be < E;   // always true for finite inputs and k <= E
       const int owner = ok ? (be & 63) : 0, slot = ok ? (be >> 6) : 0;
       float pp = 0.0f;
@@ -142,7 +150,7 @@ template <int EPW, int TPW, int KS, int U>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
   constexpr int EW = 4 / KS;
   constexpr int E_PAD = 16 * EPW * EW;
   constexpr int BT = 16 * TPW;
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, psum, cnt);
+  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -254,7 +262,7 @@ template <int E_PAD>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
   constexpr int BT = 16;
   constexpr int NV = (E_PAD + 63) / 64;
   __shared__ float lg[BT][E_PAD];
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, psum, cnt);
+  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -321,8 +329,8 @@ RoutePlan route_plan(const moe_desc_t& d) {
 }
 
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
-                        const float* bias, int32_t* topk_idx, float* topk_w, float* p_part,
-                        int32_t* cnt_part, hipStream_t s) {
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
+                        float* p_part, int32_t* cnt_part, hipStream_t s) {
   const RoutePlan rp = route_plan(d);
   if (rp.n_blocks == 0) return hipSuccess;
   const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts, k = (int)d.top_k;
@@ -333,7 +341,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
 #define MOE_ROUTE_F32(EP)                                                                     \
   if (rp.E_pad == EP) {                                                                       \
     hipLaunchKernelGGL(route_f32_kernel<EP>, grid, block, 0, s, xx, ww, bias, T, dm, E, k,    \
-                       topk_idx, topk_w, p_part, cnt_part);                                   \
+                       topk_idx, topk_w, gap, p_part, cnt_part);                              \
     return hipGetLastError();                                                                 \
   }
     MOE_ROUTE_F32(64)
@@ -350,7 +358,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
     constexpr int U_ = (EPW_ + TPW_) <= 2 ? 4 : ((EPW_ + TPW_) <= 4 ? 2 : 1);                 \
     hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, U_>), grid, block, 0, s, xx, ww,   \
-                       bias, T, dm, E, k, topk_idx, topk_w, p_part, cnt_part);                \
+                       bias, T, dm, E, k, topk_idx, topk_w, gap, p_part, cnt_part);           \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTE_BF16(1, 1, 4)

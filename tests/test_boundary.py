@@ -109,7 +109,7 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     # NULL descriptor / NULL tensors
     assert L.moe_forward(None, fake, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
     assert L.moe_forward(ctypes.byref(d), None, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
-    assert L.moe_route(ctypes.byref(d), fake, fake, None, None, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_route(ctypes.byref(d), fake, fake, None, None, fake, None, None, None, fake, ws_need, None) == 1
     assert L.moe_dispatch(ctypes.byref(d), fake, fake, None, fake, fake, fake, ws_need, None) == 1
     assert L.moe_experts(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, None, fake, ws_need, None) == 1
     assert L.moe_combine(ctypes.byref(d), fake, fake, None, fake, None) == 1

@@ -58,10 +58,18 @@ def case(request):
 
 def test_route(case):
     name, wl, inp, dinp, ref = case
-    idx, w, f, p = moe.route(dinp["x"], dinp["W_router"], dinp["router_bias"], wl.k)
+    idx, w, f, p, gap = moe.route(dinp["x"], dinp["W_router"], dinp["router_bias"], wl.k,
+                                  want_gap=True)
     torch.cuda.synchronize()
-    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    idx, w, gap = idx.cpu().numpy(), w.cpu().numpy(), gap.cpu().numpy()
     check_routing(idx, w, ref["route"])
+    # gap = s_(k) - s_(k+1) of the selection scores (+inf when k == E)
+    srt = -np.sort(-ref["route"]["s"].astype(np.float64), axis=1)
+    gap_ref = srt[:, wl.k - 1] - srt[:, wl.k] if wl.k < wl.E else np.full(wl.T, np.inf)
+    if wl.k < wl.E:
+        np.testing.assert_allclose(gap, gap_ref, rtol=0, atol=1e-5)
+    else:
+        assert np.all(np.isposinf(gap))
     f_ref, p_ref = oracle.aux_stats(ref["route"]["p"], idx, wl.E)   # f of the GPU's valid routing
     np.testing.assert_allclose(f.cpu().numpy(), f_ref, atol=STAT_TOL, rtol=0)
     np.testing.assert_allclose(p.cpu().numpy(), p_ref, atol=STAT_TOL, rtol=0)
