@@ -220,7 +220,8 @@ constexpr size_t KERNEL_LDS_BYTES =
 template <int NB, bool GATED, int P>
 __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t* smem, int g,
                                                       int64_t row_begin, int M, int m0,
-                                                      int ncol0, int k0, int nk, void* outp) {
+                                                      int ncol0, int k0, int nk, int rot,
+                                                      void* outp) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
   static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
   constexpr int MB = 2, BMT = 64, STAGE = BMT * LDK, NL = 4 * NB;   // NL: B loads per step
@@ -278,15 +279,17 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
   u32x4 rb[P][NL];   // weights of steps in flight: set q holds step t with t % P == q
   u32x4 ra[MB];
 
+  // Step t reads K step (t + rot) mod nk (see k_rotation).
+#define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
 #define MOE_SLOAD_B(q, t)                                                                  \
   _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
-    rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + min((t), nk - 1) * BK);
+    rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + MOE_KSTEP(t) * BK);
 #define MOE_SSTORE_B(q, st)                                                                \
   _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
     *reinterpret_cast<u32x4*>(Bw + (st) * SB_STAGE + bst[j]) = rb[q][j];
 #define MOE_SLOAD_A(t)                                                                     \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
-    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (t) * BK);
+    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + MOE_KSTEP(t) * BK);
 #define MOE_SSTORE_A(st)                                                                   \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
     *reinterpret_cast<u32x4*>(smem + (st) * STAGE + (lr + 32 * i) * LDK + lc) = ra[i];
@@ -332,6 +335,7 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 #pragma unroll
     for (int u = 0; u < P; ++u) MOE_SSTEP(kt + u, (u + 1) % P);   // (u: the macros use j)
   }
+#undef MOE_KSTEP
 #undef MOE_SLOAD_B
 #undef MOE_SSTORE_B
 #undef MOE_SLOAD_A
@@ -344,7 +348,7 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 template <int MB, int NB, bool GATED>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
                                                int64_t row_begin, int M, int m0, int ncol0,
-                                               int k0, int nk, void* outp) {
+                                               int k0, int nk, int rot, void* outp) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
   constexpr int BMT = 32 * MB;
   constexpr int STAGE = BMT * LDK;
@@ -394,13 +398,15 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
   bf16x8 b0[NB][4], b1[NB][4], b2[NB][4];   // three B register sets (nb, k16 step)
   u32x4 ra[MB];
 
+  // Step t reads K step (t + rot) mod nk (see k_rotation).
+#define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
 #define MOE_LOAD_B(set, t)                                                                 \
   _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                        \
     _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
-      set[nb][s] = *reinterpret_cast<const bf16x8*>(pb[nb] + min((t), nk - 1) * BK + 8 * s);
+      set[nb][s] = *reinterpret_cast<const bf16x8*>(pb[nb] + MOE_KSTEP(t) * BK + 8 * s);
 #define MOE_LOAD_A(t)                                                                      \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
-    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (t) * BK);
+    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + MOE_KSTEP(t) * BK);
 #define MOE_STORE_A(st)                                                                    \
   {                                                                                        \
     bf16_t* As_ = smem + (st) * STAGE;                                                     \
@@ -470,6 +476,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     MOE_STEP(kt + 1, b1, b0);
     MOE_STEP(kt + 2, b2, b1);
   }
+#undef MOE_KSTEP
 #undef MOE_LOAD_B
 #undef MOE_LOAD_A
 #undef MOE_STORE_A
@@ -480,6 +487,17 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #undef MOE_STEP
 
   store_tile<MB, NB, GATED>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol);
+}
+
+// First K step of a tile: tiles running at the same time start at different K offsets, so
+// their weight streams spread over the HBM channels instead of all reading the same column
+// range of rows at a common stride.  A function of the expert and the output columns only
+// (in units of the large tiles' width, whatever the tile kind), so the summation order of
+// an output element does not depend on the rest of the batch.
+template <bool GATED>
+__device__ inline int k_rotation(int g, int ncol0, int nk) {
+  const unsigned cb = (unsigned)ncol0 / (GATED ? 128u : 256u);
+  return (int)((cb + 13u * (unsigned)g) % (unsigned)nk);
 }
 
 // One work unit: (K half, tile) of the table built in LDS.
@@ -502,21 +520,22 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   const int mt = local % mt_g;
   const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
   const int rows = m_tile_rows(M, mt);
+  const int rot = k_rotation<GATED>(g, ncol0, nk);
   if (!sm && rows == BM_BIG)
     gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
-                                          outp);
+                                          rot, outp);
   else if (!sm && rows == 128)
     gemm_bf16_tile<128 / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
-                                       outp);
+                                       rot, outp);
   else if (!sm)
     gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
-                                            nk, outp);
+                                            nk, rot, outp);
   else if (GATED || !narrow)
     gemm_bf16_tile_stream<2, GATED, STREAM_P2>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                               k0, nk, outp);
+                                               k0, nk, rot, outp);
   else if constexpr (!GATED)
     gemm_bf16_tile_stream<1, GATED, STREAM_P1>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                               k0, nk, outp);
+                                               k0, nk, rot, outp);
 }
 
 // Persistent kernel over the work units in table order (group, n-tile, m-tile), dealt to
