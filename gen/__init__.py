@@ -13,6 +13,12 @@ weights, d_ff for the down weights), then rounded to bfloat16 with round-to-near
 Layouts (all row-major, ``nn.Linear``'s out x in convention for weights):
   x [T, d]; W_router [E, d]; router_bias [E] float32 or None;
   W_gate, W_up [E + S, F, d]; W_down [E + S, d, F]  (S = 1 appends the shared expert).
+
+Workloads with 8-bit expert weights draw the same bf16 weights and store them as
+``Wq_gate``, ``Wq_up``, ``Wq_down`` (uint8 e4m3 "fn" codes, same shapes) with one float32
+scale per output row (``s_gate``, ``s_up`` [E + S, F]; ``s_down`` [E + S, d]): scale =
+max |row| / 448, codes = the row divided by its scale, cast with ``torch.float8_e4m3fn``
+(round to nearest even); the bf16 tensors are then dropped.  x and the router stay bf16.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ class Workload:
     dtype: str = "bf16"               # "bf16" or "f32" for x and all weights
     bias_range: float = 0.0           # > 0: selection bias ~ U(-r, r)
     row_scales: tuple | None = None   # per-expert router row scale (load skew)
+    weights: str = "same"             # "same" (as dtype) or "fp8": e4m3 expert weights
     recipe: str = ""
 
     def replace(self, **kw) -> "Workload":
@@ -83,6 +90,14 @@ WORKLOADS = {
         recipe="x~N(0,1); weights N(0,1/fan_in) bf16; router row scales calibrated so "
                "top-1 loads follow Zipf(1.1); capacity factor 1.25"),
 }
+
+
+WORKLOADS["mixtral_decode_fp8"] = WORKLOADS["mixtral_decode"].replace(
+    name="mixtral_decode_fp8", weights="fp8",
+    recipe=WORKLOADS["mixtral_decode"].recipe + "; expert weights e4m3 with per-row scales")
+WORKLOADS["switch_capacity_fp8"] = WORKLOADS["switch_capacity"].replace(
+    name="switch_capacity_fp8", weights="fp8",
+    recipe=WORKLOADS["switch_capacity"].recipe + "; expert weights e4m3 with per-row scales")
 
 
 def _chunk_seed(seed: int, tid: int, chunk: int) -> int:
@@ -141,7 +156,27 @@ def make_inputs(wl: Workload, seed: int = 0, threads: int | None = None,
         if wl.row_scales is not None:
             out["W_router"].mul_(torch.tensor(wl.row_scales, dtype=torch.float32)[:, None])
         out["W_router"] = out["W_router"].to(dt)
+    if wl.weights == "fp8":
+        for name in ("W_gate", "W_up", "W_down"):
+            if name in out:
+                q, sc = _to_e4m3_rows(out.pop(name))
+                out["Wq_" + name[2:]], out["s_" + name[2:]] = q, sc
     return out
+
+
+def _to_e4m3_rows(W: torch.Tensor):
+    """Per-row 8-bit storage of W [G, N, K]: (codes uint8 [G, N, K], scales f32 [G, N])."""
+    G, N, K = W.shape
+    q = torch.empty((G, N, K), dtype=torch.uint8)
+    sc = torch.empty((G, N), dtype=torch.float32)
+    for g in range(G):
+        w = W[g].to(torch.float32)
+        amax = w.abs().amax(dim=1)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        v = (w / s[:, None]).clamp_(-448.0, 448.0)
+        q[g] = v.to(torch.float8_e4m3fn).view(torch.uint8)
+        sc[g] = s
+    return q, sc
 
 
 def workload(name: str) -> Workload:

@@ -29,7 +29,13 @@ notes of the repository):
   * f_e counts top-k assignments before any capacity drop and is normalised by T*k;
   * capacity C = max(floor(cf * k * T / E), k); assignments are ranked per expert in
     row-major (token, slot) order and the first C are kept;
-  * a dropped assignment contributes zero; the layer adds no residual.
+  * a dropped assignment contributes zero; the layer adds no residual;
+  * 8-bit expert weights (an extension past the pages' layer: [book ch.30] 30.4.6 counts
+    FP8 among the measures that halve the memory traffic of each operation, and
+    [MoE practice], section on quantisation and routing, keeps the router in high
+    precision while the expert weights take the quantisation) are e4m3 "fn" codes with
+    one float32 scale per output row, dequantised exactly before the same arithmetic;
+    the router, x and h stay as in the bf16 layer.
 
 Pins: tests/test_oracle_pins.py checks each function against values the pages print,
 closed forms, library routines and brute force.  Large-shape absolute values are
@@ -55,6 +61,29 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(a, dtype=F32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
     return u.astype(np.uint32).view(F32)
+
+
+def e4m3_decode(q) -> np.ndarray:
+    """Value of each 8-bit float in the e4m3 "fn" encoding; returns float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent (bias 7), bits 2..0 the mantissa.  An
+    exponent field of 0 is subnormal: m/8 * 2^-6.  Otherwise (1 + m/8) * 2^(e - 7),
+    except that e = 15 with m = 7 is NaN (the encoding has no infinities, so the
+    largest finite value is 1.75 * 2^8 = 448).
+    """
+    q = np.asarray(q, np.uint8).astype(np.int64)
+    sign = np.where(q & 0x80, -1.0, 1.0)
+    e = (q >> 3) & 0xF
+    m = (q & 0x7).astype(F64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(F64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def dequant_rows(q, scale) -> np.ndarray:
+    """Weights stored as e4m3 codes with one float32 scale per output row:
+    W[n, :] = scale[n] * decode(q[n, :]), in float64 (exact: no rounding happens)."""
+    return np.asarray(scale, F64)[:, None] * e4m3_decode(q)
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -239,6 +268,19 @@ def _np(a):
     return np.asarray(a, F32)
 
 
+def expert_weights(inputs: dict, e: int):
+    """(W_gate[e], W_up[e], W_down[e]) of expert e.  With 8-bit expert weights (inputs
+    holding Wq_gate, Wq_up, Wq_down as e4m3 codes and s_gate, s_up, s_down as per-row
+    scales) they are dequantised exactly in float64; otherwise widened from float32."""
+    if "Wq_gate" in inputs:
+        q = lambda name: np.asarray(inputs[name][e].numpy() if hasattr(inputs[name], "numpy")
+                                    else inputs[name][e], np.uint8)
+        sc = lambda name: _np(inputs[name][e])
+        return (dequant_rows(q("Wq_gate"), sc("s_gate")), dequant_rows(q("Wq_up"), sc("s_up")),
+                dequant_rows(q("Wq_down"), sc("s_down")))
+    return (_np(inputs["W_gate"][e]), _np(inputs["W_up"][e]), _np(inputs["W_down"][e]))
+
+
 def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
             h_bf16: bool = True, idx_override=None) -> dict:
     """The whole layer: route -> stats -> dispatch -> grouped experts -> combine.
@@ -266,12 +308,10 @@ def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 
         if hi == lo:
             continue
         tok = disp["perm_src"][lo:hi] // k
-        Y[lo:hi] = expert_ffn(x[tok], _np(inputs["W_gate"][e]), _np(inputs["W_up"][e]),
-                              _np(inputs["W_down"][e]), h_bf16)
+        Y[lo:hi] = expert_ffn(x[tok], *expert_weights(inputs, e), h_bf16)
     shared = None
     if n_shared:
-        shared = expert_ffn(x, _np(inputs["W_gate"][E]), _np(inputs["W_up"][E]),
-                            _np(inputs["W_down"][E]), h_bf16)
+        shared = expert_ffn(x, *expert_weights(inputs, E), h_bf16)
     y = combine(T, d, r["w"], disp["slot_pos"], Y, shared)
     return {"y": y, "f": f, "p": P, "route": r, "dispatch": disp, "C": C}
 
@@ -299,10 +339,8 @@ def forward_rows(inputs: dict, rows, k: int, capacity_factor: float = 0.0,
     y = np.zeros((rows.size, d), F64)
     for e in np.unique(idx[sp >= 0]):
         sel = np.argwhere((idx == e) & (sp >= 0))        # (row-in-sample, slot)
-        o = expert_ffn(x[rows[sel[:, 0]]], _np(inputs["W_gate"][e]),
-                       _np(inputs["W_up"][e]), _np(inputs["W_down"][e]), h_bf16)
+        o = expert_ffn(x[rows[sel[:, 0]]], *expert_weights(inputs, int(e)), h_bf16)
         y[sel[:, 0]] += w[sel[:, 0], sel[:, 1]].astype(F64)[:, None] * o.astype(F64)
     if n_shared:
-        y += expert_ffn(x[rows], _np(inputs["W_gate"][E]), _np(inputs["W_up"][E]),
-                        _np(inputs["W_down"][E]), h_bf16).astype(F64)
+        y += expert_ffn(x[rows], *expert_weights(inputs, E), h_bf16).astype(F64)
     return y.astype(F32)

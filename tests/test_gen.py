@@ -62,3 +62,24 @@ def test_switch_loads_follow_zipf_and_capacity_drops():
     assert abs(share[0] - pi[0]) < 0.03
     kept = np.minimum(c, C).sum()
     assert 0.40 < 1 - kept / c.sum() < 0.60     # about half of the tokens overflow
+
+
+def test_fp8_workload_stores_codes_and_row_scales():
+    """8-bit workloads replace the expert weights by e4m3 codes and per-row scales; the
+    largest code of each row decodes to 448 (scale = row max / 448), and the row
+    decodes back to the bf16 weights within half a step: 2^-4 relative for normal codes,
+    half the subnormal step (2^-10 of the scale) below them."""
+    wl = gen.workload("mixtral_decode_fp8").replace(T=4, d=64, F=128)
+    inp = gen.make_inputs(wl)
+    ref = gen.make_inputs(wl.replace(weights="same"))
+    assert "W_gate" not in inp and inp["Wq_gate"].dtype == torch.uint8
+    assert inp["Wq_gate"].shape == (wl.E, wl.F, wl.d) and inp["s_gate"].shape == (wl.E, wl.F)
+    assert inp["Wq_down"].shape == (wl.E, wl.d, wl.F) and inp["s_down"].shape == (wl.E, wl.d)
+    for name in ("gate", "up", "down"):
+        vals = inp["Wq_" + name].view(torch.float8_e4m3fn).to(torch.float32)
+        assert torch.equal(vals.abs().amax(dim=2), torch.full(vals.shape[:2], 448.0))
+        W = ref["W_" + name].to(torch.float32)
+        deq = vals * inp["s_" + name][..., None]
+        bound = torch.maximum(W.abs() * 2.0 ** -4, inp["s_" + name][..., None] * 2.0 ** -10)
+        assert ((deq - W).abs() <= bound * (1 + 1e-6)).all()
+    assert torch.equal(inp["x"], ref["x"]) and torch.equal(inp["W_router"], ref["W_router"])

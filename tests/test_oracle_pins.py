@@ -397,3 +397,81 @@ def test_planted_mistakes_are_caught(monkeypatch):
         m.setattr(mo, "combine", lambda T, d, w, sp, Y, shared=None:
                   orig_combine(T, d, np.ones_like(w), sp, Y, shared))
         assert _pins_fail(test_identical_experts_reduce_to_dense_ffn)
+
+
+# ------------------------------------------------------------------ 8-bit expert weights
+def test_e4m3_decode_matches_torch_for_every_code():
+    """The oracle's e4m3 decoder (written from the format definition) against the
+    library's float8_e4m3fn conversion, for all 256 codes (NaN where it is NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (mine == lib) | (np.isnan(mine) & np.isnan(lib))
+    assert same.all(), codes[~same]
+
+
+def test_e4m3_decode_fixed_values():
+    """Values fixed by the encoding: 1.0, the largest finite value 448, the smallest
+    subnormal 2^-9, the smallest normal 2^-6, the largest subnormal 7/8 * 2^-6, signs,
+    and the two NaN codes."""
+    v = oracle.e4m3_decode(np.array([0x00, 0x38, 0x7E, 0x01, 0x08, 0x07, 0xB8, 0x80, 0x40],
+                                    np.uint8))
+    assert list(v) == [0.0, 1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 7 / 8 * 2.0 ** -6, -1.0, 0.0, 2.0]
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def _fp8_small(T, d, E, k, F, S=0, seed=0, bias=0.0):
+    """make_small with the expert weights stored as per-row e4m3 codes and scales."""
+    inp = make_small(T, d, E, k, F, S, seed, bias)
+    for name in ("W_gate", "W_up", "W_down"):
+        W = torch.from_numpy(inp.pop(name))
+        s = (W.abs().amax(dim=2) / 448.0).to(torch.float32)
+        q = (W / s[..., None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        inp["Wq_" + name[2:]], inp["s_" + name[2:]] = q.numpy(), s.numpy()
+    return inp
+
+
+def _fp8_dequant_torch(inp, name, e):
+    q = torch.from_numpy(np.ascontiguousarray(inp["Wq_" + name][e]))
+    s = torch.from_numpy(np.ascontiguousarray(inp["s_" + name][e])).to(torch.float64)
+    return (q.view(torch.float8_e4m3fn).to(torch.float64) * s[:, None]).numpy()
+
+
+def test_fp8_expert_weights_are_scale_times_code():
+    """W[n, :] = s[n] * decode(q[n, :]) exactly (library decode, float64 product)."""
+    inp = _fp8_small(4, 16, 3, 1, 24, S=1, seed=11)
+    for e in range(4):
+        for name, got in zip(("gate", "up", "down"), oracle.expert_weights(inp, e)):
+            np.testing.assert_array_equal(got, _fp8_dequant_torch(inp, name, e))
+
+
+@pytest.mark.parametrize("T,d,E,k,F,S,cf,bias", [
+    (24, 16, 6, 2, 20, 0, 0.0, 0.0),
+    (40, 16, 8, 3, 12, 1, 1.25, 0.05),
+])
+def test_fp8_forward_matches_per_token_loop(T, d, E, k, F, S, cf, bias):
+    """The layer with 8-bit expert weights equals the independent per-token loop run on
+    the weights the library decodes."""
+    inp = _fp8_small(T, d, E, k, F, S, seed=T + d, bias=bias)
+    out = oracle.forward(inp, k, cf, S, h_bf16=True)
+    deq = {key: v for key, v in inp.items() if not key.startswith(("Wq_", "s_"))}
+    for name in ("gate", "up", "down"):
+        deq["W_" + name] = np.stack([_fp8_dequant_torch(inp, name, e) for e in range(E + S)])
+    ref = per_token_loop(deq, k, S, cf, True)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-5, atol=1e-6)
+
+
+def test_fp8_planted_mistakes_are_caught(monkeypatch):
+    """An exponent bias of 8 instead of 7, or scales applied per input column instead of
+    per output row, fail the pins above."""
+    orig = mo.e4m3_decode
+    with monkeypatch.context() as m:
+        m.setattr(mo, "e4m3_decode", lambda q: orig(q) / 2.0)
+        m.setattr(oracle, "e4m3_decode", mo.e4m3_decode)
+        assert _pins_fail(test_e4m3_decode_fixed_values)
+        assert _pins_fail(test_e4m3_decode_matches_torch_for_every_code)
+    with monkeypatch.context() as m:
+        m.setattr(mo, "dequant_rows",
+                  lambda q, s: np.resize(np.asarray(s, np.float64), q.shape[1])[None, :]
+                  * orig(q))
+        assert _pins_fail(test_fp8_expert_weights_are_scale_times_code)
