@@ -169,6 +169,39 @@ moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32
                               const void* W_down, float* Yp, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ---- 8-bit expert weights ("Chapter 30", 30.4.6: FP8 halves the bytes each operation
+ * moves; "Mixture-of-experts in practice", section on quantisation and routing: the router
+ * stays in high precision, the expert weights carry the quantisation).
+ * The expert weights are e4m3 codes (the "fn" encoding: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, largest finite value 448) with one float32 scale per
+ * output row:  W[e][n][:] = s[e][n] * decode(Wq[e][n][:]).
+ *   Wq_gate, Wq_up [E + S, F, d] uint8;  s_gate, s_up [E + S, F] float32
+ *   Wq_down        [E + S, d, F] uint8;  s_down      [E + S, d] float32
+ * x, W_router and the activations stay in desc->dtype, which must be MOE_DTYPE_BF16
+ * (else MOE_E_UNSUPPORTED); the codes are widened exactly to bf16 for the MFMAs and the
+ * scales are applied to the fp32 sums (h = SiLU(s_g * (x.q_g)) * (s_u * (x.q_u)), o =
+ * s_d * (h.q_d)).  Workspace, streams, layouts of the other tensors and the error rules are
+ * those of the bf16 entry points; the code arrays must be 16-byte aligned, the scale arrays
+ * 4-byte aligned, and a NULL scale array for given codes is MOE_E_NULL. */
+moe_status_t moe_forward_fp8(const moe_desc_t* desc, const void* x, const void* W_router,
+                             const float* router_bias, const uint8_t* Wq_gate,
+                             const uint8_t* Wq_up, const uint8_t* Wq_down, const float* s_gate,
+                             const float* s_up, const float* s_down, void* out, float* f,
+                             float* p, void* workspace, size_t workspace_bytes, void* stream);
+moe_status_t moe_experts_fp8(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                             const int32_t* offsets, const uint8_t* Wq_gate,
+                             const uint8_t* Wq_up, const uint8_t* Wq_down, const float* s_gate,
+                             const float* s_up, const float* s_down, float* Yp, void* H,
+                             void* workspace, size_t workspace_bytes, void* stream);
+moe_status_t moe_experts_gate_up_fp8(const moe_desc_t* desc, const void* x,
+                                     const int32_t* perm_src, const int32_t* offsets,
+                                     const uint8_t* Wq_gate, const uint8_t* Wq_up,
+                                     const float* s_gate, const float* s_up, void* H,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+moe_status_t moe_experts_down_fp8(const moe_desc_t* desc, const void* H, const int32_t* offsets,
+                                  const uint8_t* Wq_down, const float* s_down, float* Yp,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Weighted combine back to token order ("Chapter 30", 30.6.1 and 30.4.5):
  *   out[t] = sum_{j ascending, slot_pos[t*k+j] >= 0} topk_w[t,j] * Yp[slot_pos[t*k+j]]
  *            + (n_shared ? Yp[T*k + t] : 0)

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_UNSUPPORTED"
           4: "MOE_E_WORKSPACE", 5: "MOE_E_HIP"}
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_capacity",
            "moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_experts_gate_up",
-           "moe_experts_down", "moe_combine")
+           "moe_experts_down", "moe_combine", "moe_forward_fp8", "moe_experts_fp8",
+           "moe_experts_gate_up_fp8", "moe_experts_down_fp8")
 
 
 class MoeDesc(ctypes.Structure):
@@ -80,6 +81,14 @@ def lib():
         L.moe_experts_down.argtypes = [D, P, P, P, P, P, S, P]
         L.moe_combine.restype = I
         L.moe_combine.argtypes = [D, P, P, P, P, P]
+        L.moe_forward_fp8.restype = I
+        L.moe_forward_fp8.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_experts_fp8.restype = I
+        L.moe_experts_fp8.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_experts_gate_up_fp8.restype = I
+        L.moe_experts_gate_up_fp8.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_experts_down_fp8.restype = I
+        L.moe_experts_down_fp8.argtypes = [D, P, P, P, P, P, P, S, P]
         _lib = L
     return _lib
 
@@ -183,6 +192,82 @@ def forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor=0
                            _ptr(ws), ws.numel(), _stream(dev))
     _check("moe_forward", st)
     return out, f, p
+
+
+def _require_fp8(q, s, name, dev, shape):
+    _require(q, "Wq_" + name, dev, torch.uint8, shape)
+    _require(s, "s_" + name, dev, torch.float32, shape[:2])
+
+
+def forward_fp8(x, W_router, router_bias, Wq_gate, Wq_up, Wq_down, s_gate, s_up, s_down, k,
+                capacity_factor=0.0, out=None, f=None, p=None, out_dtype=None, workspace=None,
+                want_stats=True):
+    """The whole layer with 8-bit (e4m3, per-row scale) expert weights: uint8 codes
+    Wq_* shaped like the bf16 weights, float32 scales s_gate/s_up [E+S, F], s_down
+    [E+S, d].  x and W_router bf16.  Returns (y, f, p)."""
+    dev = x.device
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = Wq_gate.shape
+    desc = make_desc(T, d, E, F, k, G - E, capacity_factor, x.dtype, out_dtype or x.dtype)
+    _require(x, "x", dev, x.dtype, (T, d))
+    _require(W_router, "W_router", dev, x.dtype, (E, d))
+    _require_fp8(Wq_gate, s_gate, "gate", dev, (G, F, d))
+    _require_fp8(Wq_up, s_up, "up", dev, (G, F, d))
+    _require_fp8(Wq_down, s_down, "down", dev, (G, d, F))
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    odt = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty(T, d, dtype=odt, device=dev)
+    if want_stats:
+        f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+        p = torch.empty(E, dtype=torch.float32, device=dev) if p is None else p
+    _require(out, "out", dev, odt, (T, d))
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_forward_fp8(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(router_bias),
+                               _ptr(Wq_gate), _ptr(Wq_up), _ptr(Wq_down), _ptr(s_gate),
+                               _ptr(s_up), _ptr(s_down), _ptr(out), _ptr(f), _ptr(p), _ptr(ws),
+                               ws.numel(), _stream(dev))
+    _check("moe_forward_fp8", st)
+    return out, f, p
+
+
+def experts_gate_up_fp8(x, perm_src, offsets, Wq_gate, Wq_up, s_gate, s_up, k, n_experts,
+                        H=None, workspace=None):
+    """Gate/up grouped GEMM on 8-bit weights.  Returns H (x.dtype)."""
+    dev = x.device
+    T, d = x.shape
+    G, F, _ = Wq_gate.shape
+    desc = make_desc(T, d, n_experts, F, k, G - n_experts, 0.0, x.dtype)
+    rows = T * k + (G - n_experts) * T
+    if H is None:
+        H = torch.empty(rows, F, dtype=x.dtype, device=dev)
+    _require(H, "H", dev, x.dtype, (rows, F))
+    _require_fp8(Wq_gate, s_gate, "gate", dev, (G, F, d))
+    _require_fp8(Wq_up, s_up, "up", dev, (G, F, d))
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    st = lib().moe_experts_gate_up_fp8(ctypes.byref(desc), _ptr(x), _ptr(perm_src),
+                                       _ptr(offsets), _ptr(Wq_gate), _ptr(Wq_up), _ptr(s_gate),
+                                       _ptr(s_up), _ptr(H), ws, wsb, _stream(dev))
+    _check("moe_experts_gate_up_fp8", st)
+    return H
+
+
+def experts_down_fp8(H, offsets, Wq_down, s_down, T, k, n_experts, Yp=None, workspace=None):
+    """Down grouped GEMM on 8-bit weights.  Returns Yp (float32)."""
+    dev = H.device
+    G, d, F = Wq_down.shape
+    desc = make_desc(T, d, n_experts, F, k, G - n_experts, 0.0, H.dtype)
+    rows = T * k + (G - n_experts) * T
+    if Yp is None:
+        Yp = torch.empty(rows, d, dtype=torch.float32, device=dev)
+    _require(Yp, "Yp", dev, torch.float32, (rows, d))
+    _require_fp8(Wq_down, s_down, "down", dev, (G, d, F))
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    st = lib().moe_experts_down_fp8(ctypes.byref(desc), _ptr(H), _ptr(offsets), _ptr(Wq_down),
+                                    _ptr(s_down), _ptr(Yp), ws, wsb, _stream(dev))
+    _check("moe_experts_down_fp8", st)
+    return Yp
 
 
 def route(x, W_router, router_bias, k, workspace=None, W_gate_shape=None, n_shared=0,

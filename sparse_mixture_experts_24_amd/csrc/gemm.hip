@@ -48,6 +48,35 @@ struct GemmArgs {
   int ksplit;             // 1, or 2: the K range in two halves, partial sums to out / out2
   void* out2;             // second partial output (ksplit == 2)
   int* ctr;               // NULL, or 8 per-XCD unit counters, zero at launch
+  const float* sc0;       // 8-bit weights: per-row scales of B0 [G, N] (else unused)
+  const float* sc1;       // 8-bit weights: per-row scales of B1 (gated)
+};
+
+// 8 e4m3 codes (bytes of lo, then hi; byte j = k-slot j) -> 8 bf16 operands.  Every e4m3
+// value is exact in bf16; the per-row scale is applied to the accumulated sums.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Weight registers of one K step: bf16 [nb][k16 step] operands, or the 32 code bytes of
+// each lane for 8-bit weights (k16 step s in bytes [8s, 8s + 8)).
+template <bool FP8, int NB>
+struct BRegs {
+  bf16x8 v[NB][4];
+  __device__ __forceinline__ bf16x8 op(int nb, int s) const { return v[nb][s]; }
+};
+template <int NB>
+struct BRegs<true, NB> {
+  u32x4 v[NB][2];
+  __device__ __forceinline__ bf16x8 op(int nb, int s) const {
+    const u32x4 q = v[nb][s >> 1];
+    return (s & 1) ? e4m3x8_to_bf16(q[2], q[3]) : e4m3x8_to_bf16(q[0], q[1]);
+  }
 };
 
 // Geometry of group g.
@@ -156,10 +185,11 @@ __device__ inline int tile_cols(bool small, int narrow_small) {
 // 4*(m/8) + m%4.  Gate/up: h = SiLU(g) * u -> bf16 into an LDS tile [BM][128 + 8] (the A
 // stages are free: every block barrier of the K loop is behind), then 16-byte row stores.
 // Down: fp32 stores of the lanes' columns.
-template <int MB, int NB, bool GATED>
+template <int MB, int NB, bool GATED, bool FP8>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[MB][NB], bf16_t* smem,
                                            void* outp, int64_t row_begin, int M, int m0,
-                                           int ncol0, int N, const int (&bcol)[NB]) {
+                                           int ncol0, int N, const int (&bcol)[NB],
+                                           const float (&scl)[NB]) {
   constexpr int BMT = 32 * MB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, fg = lane >> 5;
@@ -171,8 +201,9 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[MB][NB], bf16_t
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
-        Ht[row * HLD + 32 * w + fr] =
-            f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][NB - 1][r]);
+        const float gv = FP8 ? acc[mb][0][r] * scl[0] : acc[mb][0][r];
+        const float uv = FP8 ? acc[mb][NB - 1][r] * scl[NB - 1] : acc[mb][NB - 1][r];
+        Ht[row * HLD + 32 * w + fr] = f32_to_bf16(silu_fast(gv) * uv);
       }
     __syncthreads();
     bf16_t* H = (bf16_t*)outp;
@@ -196,9 +227,21 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[MB][NB], bf16_t
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * fg + (r & 3);
-          if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
+          if (m < M && n < N)
+            Y[(row_begin + m) * N + n] = FP8 ? acc[mb][nb][r] * scl[nb] : acc[mb][nb][r];
         }
       }
+  }
+}
+
+// Per-row weight scales of the lane's NB output columns (1 for bf16 weights).
+template <int NB, bool GATED, bool FP8>
+__device__ __forceinline__ void load_scales(const GemmArgs& a, int g, const int (&bcol)[NB],
+                                            float (&scl)[NB]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float* sc = (GATED && nb >= NB / 2) ? a.sc1 : a.sc0;
+    scl[nb] = FP8 ? sc[(int64_t)g * a.N + min(bcol[nb], a.N - 1)] : 1.0f;
   }
 }
 
@@ -217,14 +260,19 @@ constexpr size_t SMALL_LDS_BYTES =
 constexpr int STREAM_P2 = 2, STREAM_P1 = 8;
 constexpr size_t KERNEL_LDS_BYTES =
     GEMM_LDS_BYTES > SMALL_LDS_BYTES ? GEMM_LDS_BYTES : SMALL_LDS_BYTES;
-template <int NB, bool GATED, int P>
+// 8-bit weights: a K step of a row is 64 bytes, read by 4 lanes (16 rows per load); the
+// wave-private stage holds [NB*32 rows][64 bytes], 16-byte chunk c of row r at position
+// c ^ ((r/4)%4), and a fragment is one 8-byte read, converted to bf16 after the read.
+template <int NB, bool GATED, int P, bool FP8>
 __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t* smem, int g,
                                                       int64_t row_begin, int M, int m0,
                                                       int ncol0, int k0, int nk, int rot,
                                                       void* outp) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
   static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
-  constexpr int MB = 2, BMT = 64, STAGE = BMT * LDK, NL = 4 * NB;   // NL: B loads per step
+  constexpr int MB = 2, BMT = 64, STAGE = BMT * LDK;
+  constexpr int NL = FP8 ? 2 * NB : 4 * NB;     // B loads per step
+  constexpr int WB = FP8 ? 1 : 2;               // bytes per weight
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   const int fr = lane & 31, fg = lane >> 5;
@@ -250,23 +298,28 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
   }
   // B load j (j < NL): block nb = j / 4, rows r = 8 (j % 4) + lane / 8 of the block, the
   // lane's 16-byte chunk c = lane % 8; stored at chunk position c ^ ((r / 2) % 8).
-  const bf16_t* pbl[NL];
-  int bst[NL];
+  const char* pbl[NL];   // byte addresses
+  int bst[NL];           // byte offsets in the wave's stage
   int bcol[NB];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    const int nb = j / 4, r = 8 * (j % 4) + (lane >> 3), c = lane & 7;
+    const int nb = FP8 ? j / 2 : j / 4;
+    const int r = FP8 ? 16 * (j % 2) + (lane >> 2) : 8 * (j % 4) + (lane >> 3);
+    const int c = FP8 ? lane & 3 : lane & 7;
     const int n = GATED ? ncol0 + 32 * w + r : ncol0 + 32 * NB * w + 32 * nb + r;
-    const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
-    pbl[j] = base + ((int64_t)g * N + min(n, N - 1)) * K + 8 * c + k0 * BK;
-    bst[j] = (nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7));
+    const char* base = (const char*)((GATED && nb == 1) ? a.B1 : a.B0);
+    pbl[j] = base + (((int64_t)g * N + min(n, N - 1)) * K + k0 * BK) * WB + 16 * c;
+    bst[j] = FP8 ? (nb * 32 + r) * BK + 16 * (c ^ ((r >> 2) & 3))
+                 : 2 * ((nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7)));
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     bcol[nb] = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
-  int brd[4];   // fragment read offsets: row fr of a block, chunk 4 fg + s
+  int brd[4];   // fragment read offsets: row fr of a block, k16 step s of lane half fg
 #pragma unroll
-  for (int s = 0; s < 4; ++s) brd[s] = fr * BK + 8 * ((4 * fg + s) ^ ((fr >> 1) & 7));
+  for (int s = 0; s < 4; ++s)
+    brd[s] = FP8 ? fr * BK + 16 * ((2 * fg + (s >> 1)) ^ ((fr >> 2) & 3)) + 8 * (s & 1)
+                 : 2 * (fr * BK + 8 * ((4 * fg + s) ^ ((fr >> 1) & 7)));
 
   floatx16 acc[MB][NB];
 #pragma unroll
@@ -283,10 +336,10 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 #define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
 #define MOE_SLOAD_B(q, t)                                                                  \
   _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
-    rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + MOE_KSTEP(t) * BK);
+    rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + MOE_KSTEP(t) * BK * WB);
 #define MOE_SSTORE_B(q, st)                                                                \
   _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
-    *reinterpret_cast<u32x4*>(Bw + (st) * SB_STAGE + bst[j]) = rb[q][j];
+    *reinterpret_cast<u32x4*>((char*)Bw + (st) * SB_STAGE * 2 + bst[j]) = rb[q][j];
 #define MOE_SLOAD_A(t)                                                                     \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
     ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + MOE_KSTEP(t) * BK);
@@ -308,8 +361,15 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
       bf16x8 af[MB], bfr[NB];                                                              \
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
         af[mb] = *reinterpret_cast<const bf16x8*>(As_ + (mb * 32 + fr) * LDK + 32 * fg + 8 * s); \
-      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                    \
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs_ + nb * 32 * BK + brd[s]);          \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                  \
+        const char* bp_ = (const char*)Bs_ + nb * 32 * BK * WB + brd[s];                   \
+        if constexpr (FP8) {                                                               \
+          const uint2 q_ = *reinterpret_cast<const uint2*>(bp_);                           \
+          bfr[nb] = e4m3x8_to_bf16(q_.x, q_.y);                                            \
+        } else {                                                                           \
+          bfr[nb] = *reinterpret_cast<const bf16x8*>(bp_);                                 \
+        }                                                                                  \
+      }                                                                                    \
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
         _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                  \
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], \
@@ -341,11 +401,13 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 #undef MOE_SLOAD_A
 #undef MOE_SSTORE_A
 #undef MOE_SSTEP
-  store_tile<MB, NB, GATED>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol);
+  float scl[NB];
+  load_scales<NB, GATED, FP8>(a, g, bcol, scl);
+  store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
 }
 
 // One output tile over K steps [k0, k0 + nk) (the whole K unless split), into outp.
-template <int MB, int NB, bool GATED>
+template <int MB, int NB, bool GATED, bool FP8>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
                                                int64_t row_begin, int M, int m0, int ncol0,
                                                int k0, int nk, int rot, void* outp) {
@@ -377,14 +439,16 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     for (int i = 0; i < MB; ++i) aoff[i] = (base + aoff[i]) * K + lc;
   }
   // B: this lane's NB weight rows (one per n-block), 32 contiguous k per lane half
-  const bf16_t* pb[NB];
+  // (64 bytes of bf16, or 32 bytes of 8-bit codes)
+  constexpr int WB = FP8 ? 1 : 2;                    // bytes per weight
+  const char* pb[NB];
   int bcol[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
-    const bf16_t* base = (const bf16_t*)((GATED && nb == 1) ? a.B1 : a.B0);
+    const char* base = (const char*)((GATED && nb == 1) ? a.B1 : a.B0);
     bcol[nb] = n;
-    pb[nb] = base + ((int64_t)g * N + min(n, N - 1)) * K + 32 * fg + k0 * BK;
+    pb[nb] = base + (((int64_t)g * N + min(n, N - 1)) * K + 32 * fg + k0 * BK) * WB;
   }
 
   floatx16 acc[MB][NB];
@@ -395,15 +459,22 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8 b0[NB][4], b1[NB][4], b2[NB][4];   // three B register sets (nb, k16 step)
+  BRegs<FP8, NB> b0, b1, b2;   // three B register sets
   u32x4 ra[MB];
 
   // Step t reads K step (t + rot) mod nk (see k_rotation).
 #define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
 #define MOE_LOAD_B(set, t)                                                                 \
-  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                        \
-    _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
-      set[nb][s] = *reinterpret_cast<const bf16x8*>(pb[nb] + MOE_KSTEP(t) * BK + 8 * s);
+  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                      \
+    if constexpr (FP8) {                                                                   \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                        \
+        set.v[nb][h] = *reinterpret_cast<const u32x4*>(pb[nb] + MOE_KSTEP(t) * BK + 16 * h); \
+    } else {                                                                               \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s)                                        \
+        set.v[nb][s] =                                                                     \
+            *reinterpret_cast<const bf16x8*>(pb[nb] + MOE_KSTEP(t) * BK * 2 + 16 * s);     \
+    }                                                                                      \
+  }
 #define MOE_LOAD_A(t)                                                                      \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
     ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + MOE_KSTEP(t) * BK);
@@ -420,8 +491,8 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #define MOE_MFMA(af, set, s)                                                               \
   _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                      \
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], set[nb][s], acc[mb][nb], \
-                                                            0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], set.op(nb, s),          \
+                                                            acc[mb][nb], 0, 0, 0);
 #define MOE_COMPUTE(set, st)                                                               \
   {                                                                                        \
     bf16x8 fa[MB], fb[MB];                                                                 \
@@ -486,7 +557,9 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #undef MOE_INTERLEAVE
 #undef MOE_STEP
 
-  store_tile<MB, NB, GATED>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol);
+  float scl[NB];
+  load_scales<NB, GATED, FP8>(a, g, bcol, scl);
+  store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
 }
 
 // First K step of a tile: tiles running at the same time start at different K offsets, so
@@ -501,7 +574,7 @@ __device__ inline int k_rotation(int g, int ncol0, int nk) {
 }
 
 // One work unit: (K half, tile) of the table built in LDS.
-template <bool GATED>
+template <bool GATED, bool FP8>
 __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
                                                const int* tiles, int64_t ntile, int64_t unit) {
   const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
@@ -522,19 +595,19 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   const int rows = m_tile_rows(M, mt);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
   if (!sm && rows == BM_BIG)
-    gemm_bf16_tile<BM_BIG / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
+    gemm_bf16_tile<BM_BIG / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
                                           rot, outp);
   else if (!sm && rows == 128)
-    gemm_bf16_tile<128 / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
+    gemm_bf16_tile<128 / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
                                        rot, outp);
   else if (!sm)
-    gemm_bf16_tile<BM_SMALL / 32, 2, GATED>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
+    gemm_bf16_tile<BM_SMALL / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
                                             nk, rot, outp);
   else if (GATED || !narrow)
-    gemm_bf16_tile_stream<2, GATED, STREAM_P2>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+    gemm_bf16_tile_stream<2, GATED, STREAM_P2, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
                                                k0, nk, rot, outp);
   else if constexpr (!GATED)
-    gemm_bf16_tile_stream<1, GATED, STREAM_P1>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
+    gemm_bf16_tile_stream<1, GATED, STREAM_P1, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
                                                k0, nk, rot, outp);
 }
 
@@ -545,7 +618,7 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
 // With counters (a.ctr, 8 ints, zero at launch) each block takes its XCD's next unit
 // when it is free, so blocks that drew cheap tiles (a group's 64- or 128-row remainder)
 // take more, and an XCD that runs out helps the others.
-template <bool GATED>
+template <bool GATED, bool FP8>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
@@ -563,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   if (a.ctr == nullptr) {
     const int per = gridDim.x >> 3;
     for (int64_t unit = (int64_t)x * per + (blockIdx.x >> 3); unit < total; unit += gridDim.x)
-      gemm_bf16_unit<GATED>(a, smem, tiles, ntile, unit);
+      gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit);
     return;
   }
   for (;;) {
@@ -585,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int64_t unit = next_unit;
     __syncthreads();   // read by all before thread 0 writes the next one
     if (unit < 0) break;
-    gemm_bf16_unit<GATED>(a, smem, tiles, ntile, unit);
+    gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit);
   }
 }
 
@@ -681,11 +754,11 @@ static int device_cu_count() {
   return n;
 }
 
-template <bool GATED>
+template <bool GATED, bool FP8>
 static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED, FP8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)KERNEL_LDS_BYTES);
     if (e != hipSuccess) return e;
@@ -695,8 +768,8 @@ static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) 
   if (max_tiles < grid) grid = max_tiles;
   grid = round_up(grid, 8);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_bf16_kernel<GATED>, dim3((unsigned)grid), dim3(256), KERNEL_LDS_BYTES,
-                     s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<GATED, FP8>), dim3((unsigned)grid), dim3(256),
+                     KERNEL_LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -732,22 +805,25 @@ static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
 }
 
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
-                          const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
-                          int32_t* ctr, hipStream_t s) {
+                          const int32_t* offsets, const ExpertWeights& ew, void* H, int32_t* ctr,
+                          hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, offsets);
   a.A = x;
   a.perm_src = perm_src;
-  a.B0 = W_gate;
-  a.B1 = W_up;
+  a.B0 = ew.gate;
+  a.B1 = ew.up;
+  a.sc0 = ew.s_gate;
+  a.sc1 = ew.s_up;
   a.out = H;
   a.N = (int)d.d_ff;
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
   a.ksplit = 1;
   a.ctr = dynamic_tiles(d) ? ctr : nullptr;
-  return bf ? run_bf16<true>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128), s)
-            : run_f32<true>(a, max_m_tiles(d, 64), s);
+  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128);
+  if (!bf) return run_f32<true>(a, max_m_tiles(d, 64), s);
+  return ew.fp8 ? run_bf16<true, true>(a, mt, s) : run_bf16<true, false>(a, mt, s);
 }
 
 // Whether moe_forward splits the down GEMM's K range in two: when the estimated number
@@ -767,11 +843,13 @@ bool down_split_k(const moe_desc_t& d) {
 }
 
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, float* Yp2, int32_t* ctr, hipStream_t s) {
+                       const ExpertWeights& ew, float* Yp, float* Yp2, int32_t* ctr,
+                       hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, offsets);
   a.A = H;
-  a.B0 = W_down;
+  a.B0 = ew.down;
+  a.sc0 = ew.s_down;
   a.out = Yp;
   a.N = (int)d.d_model;
   a.K = (int)d.d_ff;
@@ -785,8 +863,9 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
   a.ksplit = (bf && Yp2) ? 2 : 1;
   a.out2 = Yp2;
   a.ctr = dynamic_tiles(d) ? ctr : nullptr;
-  return bf ? run_bf16<false>(a, max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128), s)
-            : run_f32<false>(a, max_m_tiles(d, 64), s);
+  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128);
+  if (!bf) return run_f32<false>(a, max_m_tiles(d, 64), s);
+  return ew.fp8 ? run_bf16<false, true>(a, mt, s) : run_bf16<false, false>(a, mt, s);
 }
 
 }  // namespace moe

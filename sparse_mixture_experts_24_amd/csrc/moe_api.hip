@@ -86,6 +86,124 @@ static int64_t capacity_of(const moe_desc_t& d) {
     if ((call) != hipSuccess) return MOE_E_HIP; \
   } while (0)
 
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+static ExpertWeights plain_weights(const void* g, const void* u, const void* dn) {
+  return ExpertWeights{g, u, dn, nullptr, nullptr, nullptr, false};
+}
+
+// 8-bit weights: a bf16 layer, and every scale array given for the weights given.
+static moe_status_t check_fp8(const moe_desc_t& d, const ExpertWeights& ew) {
+  if (!ew.fp8) return MOE_OK;
+  if (d.dtype != MOE_DTYPE_BF16) return MOE_E_UNSUPPORTED;
+  if ((ew.gate && !ew.s_gate) || (ew.up && !ew.s_up) || (ew.down && !ew.s_down))
+    return MOE_E_NULL;
+  if (!aligned4(ew.s_gate) || !aligned4(ew.s_up) || !aligned4(ew.s_down))
+    return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status_t experts_impl(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                                 const int32_t* offsets, const ExpertWeights& ew, float* Yp,
+                                 void* H, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  const bool any = d.T > 0;
+  if (!offsets || !ew.gate || !ew.up || !ew.down || (any && (!x || !perm_src || !Yp)))
+    return MOE_E_NULL;
+  if ((st = check_fp8(d, ew)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(ew.gate) || !aligned16(ew.up) || !aligned16(ew.down) ||
+      !aligned16(Yp) || (H && !aligned16(H)))
+    return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  void* h = H ? H : w.H;
+  MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
+  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, ew, h, w.ctr, s));
+  MOE_HIP(launch_down(d, h, offsets, ew, Yp, nullptr, w.ctr + 8, s));
+  return MOE_OK;
+}
+
+// Work counters of an optional workspace (NULL: static tile order).
+static moe_status_t optional_ctr(const moe_desc_t& d, void* ws, size_t bytes, int32_t** ctr) {
+  *ctr = nullptr;
+  if (!ws) return MOE_OK;
+  Workspace w;
+  const moe_status_t st = check_ws(d, ws, bytes, w);
+  if (st == MOE_OK) *ctr = w.ctr;
+  return st;
+}
+
+static moe_status_t gate_up_impl(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                                 const int32_t* offsets, const ExpertWeights& ew, void* H,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (!offsets || !ew.gate || !ew.up || (desc->T > 0 && (!x || !perm_src || !H)))
+    return MOE_E_NULL;
+  if ((st = check_fp8(*desc, ew)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(ew.gate) || !aligned16(ew.up) || !aligned16(H))
+    return MOE_E_UNSUPPORTED;
+  int32_t* ctr;
+  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctr) MOE_HIP(launch_zero_i32(ctr, 8, s));
+  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, ew, H, ctr, s));
+  return MOE_OK;
+}
+
+static moe_status_t down_impl(const moe_desc_t* desc, const void* H, const int32_t* offsets,
+                              const ExpertWeights& ew, float* Yp, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (!offsets || !ew.down || (desc->T > 0 && (!H || !Yp))) return MOE_E_NULL;
+  if ((st = check_fp8(*desc, ew)) != MOE_OK) return st;
+  if (!aligned16(H) || !aligned16(ew.down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
+  int32_t* ctr;
+  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
+  MOE_HIP(launch_down(*desc, H, offsets, ew, Yp, nullptr, ctr ? ctr + 8 : nullptr, s));
+  return MOE_OK;
+}
+
+static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const void* W_router,
+                                 const float* router_bias, const ExpertWeights& ew, void* out,
+                                 float* f, float* p, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!W_router || !ew.gate || !ew.up || !ew.down || (d.T > 0 && (!x || !out)))
+    return MOE_E_NULL;
+  if ((st = check_fp8(d, ew)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(W_router) || !aligned16(ew.gate) || !aligned16(ew.up) ||
+      !aligned16(ew.down) || !aligned16(out))
+    return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  const int64_t TK = d.T * d.top_k;
+  const int E = (int)d.n_experts;
+  const int64_t C = capacity_of(d);
+  const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
+  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, w.p_part,
+                       w.cnt_part, s));
+  MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
+                             f, p, w.ctr, kTileCounters, s));
+  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
+                         w.perm_src, w.slot_pos, s));
+  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
+  MOE_HIP(launch_down(d, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
+  MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -164,65 +282,22 @@ moe_status_t moe_experts(const moe_desc_t* desc, const void* x, const int32_t* p
                          const int32_t* offsets, const void* W_gate, const void* W_up,
                          const void* W_down, float* Yp, void* H, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  moe_status_t st = validate(desc);
-  if (st != MOE_OK) return st;
-  const moe_desc_t& d = *desc;
-  const bool any = d.T > 0;
-  if (!offsets || !W_gate || !W_up || !W_down || (any && (!x || !perm_src || !Yp)))
-    return MOE_E_NULL;
-  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
-      !aligned16(Yp) || (H && !aligned16(H)))
-    return MOE_E_UNSUPPORTED;
-  Workspace w;
-  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  void* h = H ? H : w.H;
-  MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
-  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, W_gate, W_up, h, w.ctr, s));
-  MOE_HIP(launch_down(d, h, offsets, W_down, Yp, nullptr, w.ctr + 8, s));
-  return MOE_OK;
-}
-
-// Work counters of an optional workspace (NULL: static tile order).
-static moe_status_t optional_ctr(const moe_desc_t& d, void* ws, size_t bytes, int32_t** ctr) {
-  *ctr = nullptr;
-  if (!ws) return MOE_OK;
-  Workspace w;
-  const moe_status_t st = check_ws(d, ws, bytes, w);
-  if (st == MOE_OK) *ctr = w.ctr;
-  return st;
+  return experts_impl(desc, x, perm_src, offsets, plain_weights(W_gate, W_up, W_down), Yp, H,
+                      workspace, workspace_bytes, stream);
 }
 
 moe_status_t moe_experts_gate_up(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
                                  const int32_t* offsets, const void* W_gate, const void* W_up,
                                  void* H, void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status_t st = validate(desc);
-  if (st != MOE_OK) return st;
-  if (!offsets || !W_gate || !W_up || (desc->T > 0 && (!x || !perm_src || !H)))
-    return MOE_E_NULL;
-  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(H))
-    return MOE_E_UNSUPPORTED;
-  int32_t* ctr;
-  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (ctr) MOE_HIP(launch_zero_i32(ctr, 8, s));
-  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, W_gate, W_up, H, ctr, s));
-  return MOE_OK;
+  return gate_up_impl(desc, x, perm_src, offsets, plain_weights(W_gate, W_up, nullptr), H,
+                      workspace, workspace_bytes, stream);
 }
 
 moe_status_t moe_experts_down(const moe_desc_t* desc, const void* H, const int32_t* offsets,
                               const void* W_down, float* Yp, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  moe_status_t st = validate(desc);
-  if (st != MOE_OK) return st;
-  if (!offsets || !W_down || (desc->T > 0 && (!H || !Yp))) return MOE_E_NULL;
-  if (!aligned16(H) || !aligned16(W_down) || !aligned16(Yp)) return MOE_E_UNSUPPORTED;
-  int32_t* ctr;
-  if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
-  MOE_HIP(launch_down(*desc, H, offsets, W_down, Yp, nullptr, ctr ? ctr + 8 : nullptr, s));
-  return MOE_OK;
+  return down_impl(desc, H, offsets, plain_weights(nullptr, nullptr, W_down), Yp, workspace,
+                   workspace_bytes, stream);
 }
 
 moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t* slot_pos,
@@ -240,31 +315,45 @@ moe_status_t moe_forward(const moe_desc_t* desc, const void* x, const void* W_ro
                          const float* router_bias, const void* W_gate, const void* W_up,
                          const void* W_down, void* out, float* f, float* p, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  moe_status_t st = validate(desc);
-  if (st != MOE_OK) return st;
-  const moe_desc_t& d = *desc;
-  if (!W_router || !W_gate || !W_up || !W_down || (d.T > 0 && (!x || !out))) return MOE_E_NULL;
-  if (!aligned16(x) || !aligned16(W_router) || !aligned16(W_gate) || !aligned16(W_up) ||
-      !aligned16(W_down) || !aligned16(out))
-    return MOE_E_UNSUPPORTED;
-  Workspace w;
-  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  const RoutePlan rp = route_plan(d);
-  const int64_t TK = d.T * d.top_k;
-  const int E = (int)d.n_experts;
-  const int64_t C = capacity_of(d);
-  const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
-  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, w.p_part,
-                       w.cnt_part, s));
-  MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
-                             f, p, w.ctr, kTileCounters, s));
-  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
-                         w.perm_src, w.slot_pos, s));
-  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, W_gate, W_up, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, w.H, w.offsets, W_down, w.Yp, w.Yp2, w.ctr + 8, s));
-  MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
-  return MOE_OK;
+  return forward_impl(desc, x, W_router, router_bias, plain_weights(W_gate, W_up, W_down), out,
+                      f, p, workspace, workspace_bytes, stream);
+}
+
+// ---- 8-bit expert weights
+moe_status_t moe_forward_fp8(const moe_desc_t* desc, const void* x, const void* W_router,
+                             const float* router_bias, const uint8_t* Wq_gate,
+                             const uint8_t* Wq_up, const uint8_t* Wq_down, const float* s_gate,
+                             const float* s_up, const float* s_down, void* out, float* f,
+                             float* p, void* workspace, size_t workspace_bytes, void* stream) {
+  const ExpertWeights ew{Wq_gate, Wq_up, Wq_down, s_gate, s_up, s_down, true};
+  return forward_impl(desc, x, W_router, router_bias, ew, out, f, p, workspace, workspace_bytes,
+                      stream);
+}
+
+moe_status_t moe_experts_fp8(const moe_desc_t* desc, const void* x, const int32_t* perm_src,
+                             const int32_t* offsets, const uint8_t* Wq_gate,
+                             const uint8_t* Wq_up, const uint8_t* Wq_down, const float* s_gate,
+                             const float* s_up, const float* s_down, float* Yp, void* H,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const ExpertWeights ew{Wq_gate, Wq_up, Wq_down, s_gate, s_up, s_down, true};
+  return experts_impl(desc, x, perm_src, offsets, ew, Yp, H, workspace, workspace_bytes,
+                      stream);
+}
+
+moe_status_t moe_experts_gate_up_fp8(const moe_desc_t* desc, const void* x,
+                                     const int32_t* perm_src, const int32_t* offsets,
+                                     const uint8_t* Wq_gate, const uint8_t* Wq_up,
+                                     const float* s_gate, const float* s_up, void* H,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const ExpertWeights ew{Wq_gate, Wq_up, nullptr, s_gate, s_up, nullptr, true};
+  return gate_up_impl(desc, x, perm_src, offsets, ew, H, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_experts_down_fp8(const moe_desc_t* desc, const void* H, const int32_t* offsets,
+                                  const uint8_t* Wq_down, const float* s_down, float* Yp,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const ExpertWeights ew{nullptr, nullptr, Wq_down, nullptr, nullptr, s_down, true};
+  return down_impl(desc, H, offsets, ew, Yp, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -70,13 +70,25 @@ hipError_t launch_expert_scan(int32_t* blk, int64_t nb, int E, const float* p_pa
 hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int64_t C,
                           const int32_t* blk_base, const int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
+// Expert weights as the grouped GEMMs take them: tensors of desc.dtype, or (fp8 set, bf16
+// layers only) e4m3 codes with one float32 scale per output row.
+struct ExpertWeights {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const float* s_gate;   // [E + S, F]
+  const float* s_up;     // [E + S, F]
+  const float* s_down;   // [E + S, d]
+  bool fp8;
+};
 hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
-                          const int32_t* offsets, const void* W_gate, const void* W_up, void* H,
-                          int32_t* ctr, hipStream_t s);
+                          const int32_t* offsets, const ExpertWeights& ew, void* H, int32_t* ctr,
+                          hipStream_t s);
 // Yp2 non-NULL (bf16 layers): K split in two, partial sums in Yp and Yp2.
 // ctr: NULL (static tile order) or 8 int32 work counters, zero at launch.
 hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const void* W_down, float* Yp, float* Yp2, int32_t* ctr, hipStream_t s);
+                       const ExpertWeights& ew, float* Yp, float* Yp2, int32_t* ctr,
+                       hipStream_t s);
 // Sets n int32 to zero (a kernel, so that it may sit in a captured graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 constexpr int kTileCounters = 16;   // 8 per grouped GEMM

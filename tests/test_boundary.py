@@ -26,7 +26,7 @@ def L():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -131,6 +131,16 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     odd = P(0x100004)
     assert L.moe_forward(ctypes.byref(d), odd, fake, None, fake, fake, fake, fake, None, None, fake, ws_need, None) == 3
     assert L.moe_experts_gate_up(ctypes.byref(d), odd, fake, fake, fake, fake, fake, None, 0, None) == 3
+    # 8-bit expert weights: a bf16 layer with every scale array for the codes given
+    f32 = desc(dtype=0)
+    assert L.moe_forward_fp8(ctypes.byref(f32), fake, fake, None, fake, fake, fake, fake, fake, fake, fake, None, None, fake, ws_need, None) == 3
+    assert L.moe_forward_fp8(ctypes.byref(d), fake, fake, None, fake, fake, fake, None, fake, fake, fake, None, None, fake, ws_need, None) == 1
+    assert L.moe_experts_fp8(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None, fake, None, fake, ws_need, None) == 1
+    assert L.moe_experts_gate_up_fp8(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, fake, None, 0, None) == 1
+    assert L.moe_experts_down_fp8(ctypes.byref(d), fake, fake, fake, None, fake, None, 0, None) == 1
+    assert L.moe_experts_down_fp8(ctypes.byref(d), fake, fake, fake, P(0x100002), fake, None, 0, None) == 3
+    assert L.moe_experts_down_fp8(ctypes.byref(d), fake, fake, odd, fake, fake, None, 0, None) == 3
+    assert L.moe_forward_fp8(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake, fake, fake, fake, None, None, fake, ws_need // 4, None) == 4
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):
