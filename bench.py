@@ -26,7 +26,8 @@ PEAK_F32_TFLOPS = 157.3       # fp32 vector
 PEAK_HBM_GBS = 8000.0         # HBM3E
 # Which roof bounds the dominant (gate/up) kernel for each workload.
 BOUND = {"mixtral_prefill": "mfma", "fine_grained_shared": "mfma", "mixtral_decode": "hbm",
-         "switch_capacity": "hbm", "tiny_f32": "alu"}
+         "switch_capacity": "hbm", "tiny_f32": "alu", "mixtral_decode_fp8": "hbm",
+         "switch_capacity_fp8": "hbm"}
 
 
 def log(*a):
@@ -73,9 +74,9 @@ def main():
     log(f"[bench] inputs drawn and resident in HBM ({time.time() - t0:.1f}s)")
 
     T, d, E, k, F, S = wl.T, wl.d, wl.E, wl.k, wl.F, wl.n_shared
+    fp8 = wl.weights == "fp8"     # e4m3 expert weights with per-row scales
     out_dtype = wl.torch_dtype
-    desc = moe.desc_for(dinp["x"], dinp["W_router"], dinp["W_gate"], k, wl.capacity_factor,
-                        out_dtype)
+    desc = moe.make_desc(T, d, E, F, k, S, wl.capacity_factor, wl.torch_dtype, out_dtype)
     ws = moe.alloc_workspace(desc, dev)
     out = torch.empty(T, d, dtype=out_dtype, device=dev)
     f = torch.empty(E, dtype=torch.float32, device=dev)
@@ -85,12 +86,19 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     dref = ctypes.byref(desc)
-    fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]),
-                P(dinp["W_gate"]), P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p),
-                P(ws), ws.numel(), sp)
+    if fp8:
+        W8 = [P(dinp[n]) for n in ("Wq_gate", "Wq_up", "Wq_down", "s_gate", "s_up", "s_down")]
+        fwd_fn = L.moe_forward_fp8
+        fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]), *W8,
+                    P(out), P(f), P(p), P(ws), ws.numel(), sp)
+    else:
+        fwd_fn = L.moe_forward
+        fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]),
+                    P(dinp["W_gate"]), P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p),
+                    P(ws), ws.numel(), sp)
 
     def step():
-        st = L.moe_forward(*fwd_args)
+        st = fwd_fn(*fwd_args)
         if st:
             raise moe.MoeError("moe_forward", st)
 
@@ -125,11 +133,17 @@ def main():
                                       ws.numel(), sp)),
         ("dispatch", lambda: L.moe_dispatch(dref, P(idx), P(counts), P(offsets), P(perm),
                                             P(slot), P(ws), ws.numel(), sp)),
-        ("gate_up", lambda: L.moe_experts_gate_up(dref, P(dinp["x"]), P(perm), P(offsets),
-                                                  P(dinp["W_gate"]), P(dinp["W_up"]), P(H),
-                                                  P(ws), ws.numel(), sp)),
-        ("down", lambda: L.moe_experts_down(dref, P(H), P(offsets), P(dinp["W_down"]), P(Yp),
-                                            P(ws), ws.numel(), sp)),
+        ("gate_up", (lambda: L.moe_experts_gate_up_fp8(
+            dref, P(dinp["x"]), P(perm), P(offsets), P(dinp["Wq_gate"]), P(dinp["Wq_up"]),
+            P(dinp["s_gate"]), P(dinp["s_up"]), P(H), P(ws), ws.numel(), sp)) if fp8 else
+         (lambda: L.moe_experts_gate_up(dref, P(dinp["x"]), P(perm), P(offsets),
+                                        P(dinp["W_gate"]), P(dinp["W_up"]), P(H), P(ws),
+                                        ws.numel(), sp))),
+        ("down", (lambda: L.moe_experts_down_fp8(
+            dref, P(H), P(offsets), P(dinp["Wq_down"]), P(dinp["s_down"]), P(Yp), P(ws),
+            ws.numel(), sp)) if fp8 else
+         (lambda: L.moe_experts_down(dref, P(H), P(offsets), P(dinp["W_down"]), P(Yp), P(ws),
+                                     ws.numel(), sp))),
         ("combine", lambda: L.moe_combine(dref, P(Yp), P(slot), P(w), P(out2), sp)),
     ]
     for _ in range(max(1, args.warmup)):
@@ -162,13 +176,15 @@ def main():
     kept = np.diff(offs)
     N = int(offs[-1])
     touched = int(np.count_nonzero(kept)) + S
-    esz = 2 if wl.dtype == "bf16" else 4
+    esz = 2 if wl.dtype == "bf16" else 4            # activations, router
+    wsz = 1 if fp8 else esz                         # expert weights (+ f32 row scales)
     flops_gate_up = 4.0 * d * F * (N + S * T)
     flops_down = 2.0 * d * F * (N + S * T)
     flops_layer = 2.0 * T * d * E + flops_gate_up + flops_down
-    w_gate_up_bytes = touched * 2.0 * F * d * esz
+    w_gate_up_bytes = touched * 2.0 * F * (d * wsz + (4 if fp8 else 0))
     bytes_gate_up = w_gate_up_bytes + T * d * esz + (N + S * T) * F * esz
-    bytes_layer = touched * 3.0 * F * d * esz + E * d * esz + T * d * esz + T * d * esz
+    bytes_layer = (touched * (3.0 * F * d * wsz + (4.0 * (2 * F + d) if fp8 else 0.0))
+                   + E * d * esz + T * d * esz + T * d * esz)
     log(f"[bench] counts per expert: {cnt.tolist() if E <= 64 else (cnt.min(), cnt.max())}; "
         f"kept N={N} of {T * k}; experts touched {touched}")
 
@@ -185,8 +201,9 @@ def main():
                 "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = "gemm_bf16_kernel<true> (gate/up + SiLU*mul)" if wl.dtype == "bf16" else \
-        "gemm_f32_kernel<true>"
+    roof["kernel"] = ("gemm_bf16_kernel<true, true> (gate/up + SiLU*mul, e4m3 weights)" if fp8
+                      else "gemm_bf16_kernel<true> (gate/up + SiLU*mul)" if wl.dtype == "bf16"
+                      else "gemm_f32_kernel<true>")
     roof["kernel_ms"] = stage_ms["gate_up"]
     roof["algorithmic_per_launch"] = flops_gate_up if bound != "hbm" else bytes_gate_up
 
@@ -212,7 +229,8 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes and load structure of the workload)",
         "config": {"workload": wl.name, "T": T, "d_model": d, "n_experts": E, "top_k": k,
                    "d_ff": F, "n_shared": S, "capacity_factor": wl.capacity_factor,
-                   "selection_bias": wl.bias_range > 0, "out_dtype": str(out_dtype).split(".")[-1]},
+                   "selection_bias": wl.bias_range > 0, "out_dtype": str(out_dtype).split(".")[-1],
+                   "expert_weights": "e4m3 + f32 per-row scale" if fp8 else wl.dtype},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,

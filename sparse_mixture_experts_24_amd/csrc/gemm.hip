@@ -258,6 +258,12 @@ constexpr size_t SMALL_LDS_BYTES =
 // Steps of weights in flight per wave (measured on decode-sized launches: about 16 KB
 // (two-block tiles) to 32 KB (one-block down tiles) per wave is best; more is slower).
 constexpr int STREAM_P2 = 2, STREAM_P1 = 8;
+// Tiles whose group has at most 32 rows left take the barrier-free skinny tile, with 2
+// (bf16 weights) or 4 (8-bit weights: half the bytes per step) K steps in flight per wave
+// (measured on decode-sized launches; deeper is slower).
+constexpr int SKINNY_ROWS = 32;
+template <bool FP8>
+constexpr int skinny_p() { return FP8 ? 4 : 2; }
 constexpr size_t KERNEL_LDS_BYTES =
     GEMM_LDS_BYTES > SMALL_LDS_BYTES ? GEMM_LDS_BYTES : SMALL_LDS_BYTES;
 // 8-bit weights: a K step of a row is 64 bytes, read by 4 lanes (16 rows per load); the
@@ -401,6 +407,125 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 #undef MOE_SLOAD_A
 #undef MOE_SSTORE_A
 #undef MOE_SSTEP
+  float scl[NB];
+  load_scales<NB, GATED, FP8>(a, g, bcol, scl);
+  store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
+}
+
+// A tile of at most 32 rows (decode-sized groups): every wave computes all of them against
+// its own weight rows and reads its token fragments straight from global memory (the few
+// rows are L1/L2 hits), so the K loop has no block barrier and no LDS traffic for the
+// tokens.  The weights stream as in gemm_bf16_tile_stream (whole row segments per load,
+// through the wave's swizzled LDS stages); P steps of weights and tokens are in flight.
+template <int NB, bool GATED, int P, bool FP8>
+__device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t* smem, int g,
+                                                      int64_t row_begin, int M, int m0,
+                                                      int ncol0, int k0, int nk, int rot,
+                                                      void* outp) {
+  static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
+  static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
+  constexpr int MB = 1;
+  constexpr int NL = FP8 ? 2 * NB : 4 * NB;     // B loads per step
+  constexpr int WB = FP8 ? 1 : 2;               // bytes per weight
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int fr = lane & 31, fg = lane >> 5;
+  const bf16_t* A = (const bf16_t*)a.A + k0 * BK;
+  const int K = a.K, N = a.N;
+  bf16_t* Bw = smem + w * 2 * SB_STAGE;          // this wave's two B stages
+
+  // token row of this lane's fragments: row fr of the tile (rows past M read row 0 of the
+  // group; their results are never stored); lane half fg reads k 32 fg .. 32 fg + 31
+  int aoff;
+  {
+    const int m = m0 + fr < M ? m0 + fr : 0;
+    if (GATED && g < a.E) aoff = a.perm_src[row_begin + m] / a.topk * K;
+    else aoff = ((GATED ? 0 : (int)row_begin) + m) * K;
+    aoff += 32 * fg;
+  }
+  const char* pbl[NL];
+  int bst[NL];
+  int bcol[NB];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int nb = FP8 ? j / 2 : j / 4;
+    const int r = FP8 ? 16 * (j % 2) + (lane >> 2) : 8 * (j % 4) + (lane >> 3);
+    const int c = FP8 ? lane & 3 : lane & 7;
+    const int n = GATED ? ncol0 + 32 * w + r : ncol0 + 32 * NB * w + 32 * nb + r;
+    const char* base = (const char*)((GATED && nb == 1) ? a.B1 : a.B0);
+    pbl[j] = base + (((int64_t)g * N + min(n, N - 1)) * K + k0 * BK) * WB + 16 * c;
+    bst[j] = FP8 ? (nb * 32 + r) * BK + 16 * (c ^ ((r >> 2) & 3))
+                 : 2 * ((nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7)));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    bcol[nb] = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
+  int brd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    brd[s] = FP8 ? fr * BK + 16 * ((2 * fg + (s >> 1)) ^ ((fr >> 2) & 3)) + 8 * (s & 1)
+                 : 2 * (fr * BK + 8 * ((4 * fg + s) ^ ((fr >> 1) & 7)));
+
+  floatx16 acc[MB][NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][j][r] = 0.0f;
+
+  u32x4 rb[P][NL];       // weights of steps in flight: set q holds step t with t % P == q
+  bf16x8 ra[P][4];       // token fragments of the same steps (k16 steps 0..3)
+
+#define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
+#define MOE_KLOAD(q, t)                                                                    \
+  {                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < NL; ++j)                                         \
+      rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + MOE_KSTEP(t) * BK * WB);         \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
+      ra[q][s] = *reinterpret_cast<const bf16x8*>(A + aoff + MOE_KSTEP(t) * BK + 8 * s);   \
+  }
+#define MOE_KSTORE_B(q, st)                                                                \
+  _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
+    *reinterpret_cast<u32x4*>((char*)Bw + (st) * SB_STAGE * 2 + bst[j]) = rb[q][j];
+  // K step t (weights in stage t % 2, tokens in set t % P): the weights of step t+1 go from
+  // their registers into the other stage and the set is refilled with step t+1+P.  Steps
+  // t >= nk (padding to a multiple of P) multiply zero token fragments.
+#define MOE_KSTEP_BODY(t, q0, q1)                                                          \
+  {                                                                                        \
+    MOE_KSTORE_B(q1, ((t) + 1) & 1);                                                       \
+    const char* Bs_ = (const char*)Bw + ((t) & 1) * SB_STAGE * 2;                          \
+    const bool live_ = (t) < nk;                                                           \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                        \
+      const bf16x8 af_ = live_ ? ra[q0][s] : bf16x8{};                                     \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                  \
+        const char* bp_ = Bs_ + nb * 32 * BK * WB + brd[s];                                \
+        bf16x8 bfr_;                                                                       \
+        if constexpr (FP8) {                                                               \
+          const uint2 q_ = *reinterpret_cast<const uint2*>(bp_);                           \
+          bfr_ = e4m3x8_to_bf16(q_.x, q_.y);                                               \
+        } else {                                                                           \
+          bfr_ = *reinterpret_cast<const bf16x8*>(bp_);                                    \
+        }                                                                                  \
+        acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_, bfr_, acc[0][nb], 0, 0,  \
+                                                             0);                           \
+      }                                                                                    \
+    }                                                                                      \
+    MOE_KLOAD(q0, (t) + P);                                                                \
+  }
+
+  // Prologue: steps 0..P-1 requested; step 0's weights stored.  Step t's set q0 = t % P is
+  // reloaded with step t+P after its MFMAs; set q1 = (t+1) % P was requested P-1 steps ago.
+#pragma unroll
+  for (int q = 0; q < P; ++q) MOE_KLOAD(q, q);
+  MOE_KSTORE_B(0, 0);
+  const int nkp = (nk + P - 1) / P * P;
+  for (int kt = 0; kt < nkp; kt += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) MOE_KSTEP_BODY(kt + u, u, (u + 1) % P);   // (u: macros use j, s)
+  }
+#undef MOE_KSTEP
+#undef MOE_KLOAD
+#undef MOE_KSTORE_B
+#undef MOE_KSTEP_BODY
+  __syncthreads();   // every wave is done with its LDS stages before the epilogue uses LDS
   float scl[NB];
   load_scales<NB, GATED, FP8>(a, g, bcol, scl);
   store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
@@ -603,6 +728,14 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   else if (!sm)
     gemm_bf16_tile<BM_SMALL / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
                                             nk, rot, outp);
+  else if (M - mt * BM_SMALL <= SKINNY_ROWS) {
+    if (GATED || !narrow)
+      gemm_bf16_tile_skinny<2, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M, mt * BM_SMALL,
+                                                     ncol0, k0, nk, rot, outp);
+    else if constexpr (!GATED)
+      gemm_bf16_tile_skinny<1, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M, mt * BM_SMALL,
+                                                     ncol0, k0, nk, rot, outp);
+  }
   else if (GATED || !narrow)
     gemm_bf16_tile_stream<2, GATED, STREAM_P2, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
                                                k0, nk, rot, outp);

@@ -141,14 +141,14 @@ def expert_rows_reference(inp, rows, k, n_shared, h_bf16, routing, disp):
     items = []
     for e in np.unique(idx[sp >= 0]):
         sel = np.argwhere((idx == e) & (sp >= 0))
-        Wg, Wu, Wd = np32(inp["W_gate"][e]), np32(inp["W_up"][e]), np32(inp["W_down"][e])
+        Wg, Wu, Wd = oracle.expert_weights(inp, int(e))
         o, parts = oracle.expert_ffn(x[rows[sel[:, 0]]], Wg, Wu, Wd, h_bf16, return_h=True)
         for q, (i, j) in enumerate(sel):
             items.append((int(i), float(w[i, j]), int(e), int(sp[i, j]),
                           {key: v[q:q + 1] for key, v in parts.items()}, o[q:q + 1],
                           x[rows[i]:rows[i] + 1], (Wg, Wu, Wd)))
     if n_shared:
-        Wg, Wu, Wd = np32(inp["W_gate"][E]), np32(inp["W_up"][E]), np32(inp["W_down"][E])
+        Wg, Wu, Wd = oracle.expert_weights(inp, E)
         o, parts = oracle.expert_ffn(x[rows], Wg, Wu, Wd, h_bf16, return_h=True)
         for i in range(rows.size):
             items.append((i, 1.0, E, T * k + int(rows[i]),

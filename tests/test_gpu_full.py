@@ -19,7 +19,8 @@ from parity import (STAT_TOL, check_routing, check_y_rounding_aware, expert_rows
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
-FULL = ["tiny_f32", "mixtral_decode", "mixtral_prefill", "switch_capacity", "fine_grained_shared"]
+FULL = ["tiny_f32", "mixtral_decode", "mixtral_prefill", "switch_capacity", "fine_grained_shared",
+        "mixtral_decode_fp8", "switch_capacity_fp8"]
 
 
 def sample_rows(T, n, slot_pos, k, seed=0):
@@ -40,10 +41,19 @@ def test_full_size(name):
     print(f"\n[full] {name}: generating", flush=True)
     inp = gen.make_inputs(wl)
     dinp = to_dev(inp, DEV)
-    layer = moe.MoELayer(dinp["W_router"], dinp["W_gate"], dinp["W_up"], dinp["W_down"], wl.k,
-                         wl.capacity_factor, router_bias=dinp["router_bias"])
+    fp8 = wl.weights == "fp8"
     print(f"[full] {name}: forward", flush=True)
-    y, f, p = layer(dinp["x"])
+    if fp8:
+        W8 = tuple(dinp[n] for n in ("Wq_gate", "Wq_up", "Wq_down", "s_gate", "s_up", "s_down"))
+        desc = moe.make_desc(wl.T, wl.d, wl.E, wl.F, wl.k, wl.n_shared, wl.capacity_factor,
+                             wl.torch_dtype)
+        layer = None
+        y, f, p = moe.forward_fp8(dinp["x"], dinp["W_router"], dinp["router_bias"], *W8, wl.k,
+                                  wl.capacity_factor, workspace=moe.alloc_workspace(desc, DEV))
+    else:
+        layer = moe.MoELayer(dinp["W_router"], dinp["W_gate"], dinp["W_up"], dinp["W_down"],
+                             wl.k, wl.capacity_factor, router_bias=dinp["router_bias"])
+        y, f, p = layer(dinp["x"])
     idx, w, _, _ = moe.route(dinp["x"], dinp["W_router"], dinp["router_bias"], wl.k)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
@@ -75,8 +85,13 @@ def test_full_size(name):
     # at most one unit in the last place of the output type apart.
     gidx = torch.from_numpy(idx).to(DEV)
     _, offs_g, perm_g, slot_g = moe.dispatch(gidx, wl.E, wl.capacity_factor)
-    Yp, H = moe.experts(dinp["x"], perm_g, offs_g, dinp["W_gate"], dinp["W_up"],
-                        dinp["W_down"], wl.k, wl.E, want_h=True)
+    if fp8:
+        H = moe.experts_gate_up_fp8(dinp["x"], perm_g, offs_g, W8[0], W8[1], W8[3], W8[4], wl.k,
+                                    wl.E)
+        Yp = moe.experts_down_fp8(H, offs_g, W8[2], W8[5], wl.T, wl.k, wl.E)
+    else:
+        Yp, H = moe.experts(dinp["x"], perm_g, offs_g, dinp["W_gate"], dinp["W_up"],
+                            dinp["W_down"], wl.k, wl.E, want_h=True)
     y_staged = moe.combine(Yp, slot_g, w, wl.T, wl.d, wl.k, wl.n_shared,
                            out_dtype=wl.torch_dtype, n_experts=wl.E)
     torch.cuda.synchronize()
