@@ -44,7 +44,7 @@ struct GemmArgs {
   void* out;              // gated: H [rows, N] (dtype); down: Yp [rows, N] fp32
   int64_t shared_row0;    // T*k: first row of the shared expert
   int T, topk, E, G, N, K, n_tiles;
-  int narrow_small;       // down GEMM: 128-column tiles for small groups (few tiles overall)
+  int narrow_small;       // small groups take half-width tiles (gate/up 64, down 128 columns)
   int ksplit;             // 1, or 2: the K range in two halves, partial sums to out / out2
   void* out2;             // second partial output (ksplit == 2)
   int* ctr;               // NULL, or 8 per-XCD unit counters, zero at launch
@@ -178,7 +178,8 @@ __device__ inline int m_tile_rows(int M, int mt) {
 }
 template <bool GATED>
 __device__ inline int tile_cols(bool small, int narrow_small) {
-  return GATED ? 128 : ((small && narrow_small) ? 128 : 256);
+  const bool narrow = small && narrow_small;
+  return GATED ? (narrow ? 64 : 128) : (narrow ? 128 : 256);
 }
 
 // Epilogue of a tile: D[m][n] of a 32x32 block sits in lane n + 32*((m/4)%2), register
@@ -417,12 +418,17 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
 // rows are L1/L2 hits), so the K loop has no block barrier and no LDS traffic for the
 // tokens.  The weights stream as in gemm_bf16_tile_stream (whole row segments per load,
 // through the wave's swizzled LDS stages); P steps of weights and tokens are in flight.
+//
+// Gate/up with NB == 1 (64-column tiles, for launches whose tiles would leave much of a
+// last round idle): the wave's 32 weight rows are 16 gate rows and the 16 matching up rows
+// and the MFMA is taken transposed (D[weight row][token]), so a lane holds gate and up of
+// one (token, h) in registers r and r + 8.
 template <int NB, bool GATED, int P, bool FP8>
 __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t* smem, int g,
                                                       int64_t row_begin, int M, int m0,
                                                       int ncol0, int k0, int nk, int rot,
                                                       void* outp) {
-  static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
+  constexpr bool PAIRED = GATED && NB == 1;
   static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
   constexpr int MB = 1;
   constexpr int NL = FP8 ? 2 * NB : 4 * NB;     // B loads per step
@@ -450,8 +456,11 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
     const int nb = FP8 ? j / 2 : j / 4;
     const int r = FP8 ? 16 * (j % 2) + (lane >> 2) : 8 * (j % 4) + (lane >> 3);
     const int c = FP8 ? lane & 3 : lane & 7;
-    const int n = GATED ? ncol0 + 32 * w + r : ncol0 + 32 * NB * w + 32 * nb + r;
-    const char* base = (const char*)((GATED && nb == 1) ? a.B1 : a.B0);
+    const int n = PAIRED  ? ncol0 + 16 * w + (r & 15)
+                  : GATED ? ncol0 + 32 * w + r
+                          : ncol0 + 32 * NB * w + 32 * nb + r;
+    const char* base =
+        (const char*)((PAIRED ? r >= 16 : (GATED && nb == 1)) ? a.B1 : a.B0);
     pbl[j] = base + (((int64_t)g * N + min(n, N - 1)) * K + k0 * BK) * WB + 16 * c;
     bst[j] = FP8 ? (nb * 32 + r) * BK + 16 * (c ^ ((r >> 2) & 3))
                  : 2 * ((nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7)));
@@ -504,8 +513,12 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
         } else {                                                                           \
           bfr_ = *reinterpret_cast<const bf16x8*>(bp_);                                    \
         }                                                                                  \
-        acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_, bfr_, acc[0][nb], 0, 0,  \
-                                                             0);                           \
+        if constexpr (PAIRED)                                                              \
+          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr_, af_, acc[0][nb], 0, 0, \
+                                                               0);                         \
+        else                                                                               \
+          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_, bfr_, acc[0][nb], 0, 0, \
+                                                               0);                         \
       }                                                                                    \
     }                                                                                      \
     MOE_KLOAD(q0, (t) + P);                                                                \
@@ -526,9 +539,47 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
 #undef MOE_KSTORE_B
 #undef MOE_KSTEP_BODY
   __syncthreads();   // every wave is done with its LDS stages before the epilogue uses LDS
-  float scl[NB];
-  load_scales<NB, GATED, FP8>(a, g, bcol, scl);
-  store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
+  if constexpr (PAIRED) {
+    // acc[0][0][r] (r < 8): gate row 8(r/4) + 4 fg + r%4 of the wave's 16, token fr;
+    // r + 8: the matching up row.  h -> bf16 into an LDS tile [32][64 + 8], then 16-byte
+    // row stores (one per thread).
+    constexpr int HLD = 72;
+    bf16_t* Ht = smem;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t pk[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = 4 * q + 2 * i;
+        float gv[2], uv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          gv[e] = acc[0][0][r0 + e];
+          uv[e] = acc[0][0][r0 + e + 8];
+          if constexpr (FP8) {
+            const int64_t hrow = (int64_t)g * N + min(ncol0 + 16 * w + 8 * q + 4 * fg + 2 * i + e, N - 1);
+            gv[e] *= a.sc0[hrow];
+            uv[e] *= a.sc1[hrow];
+          }
+        }
+        pk[i] = (uint32_t)f32_to_bf16(silu_fast(gv[0]) * uv[0]) |
+                ((uint32_t)f32_to_bf16(silu_fast(gv[1]) * uv[1]) << 16);
+      }
+      *reinterpret_cast<uint2*>(Ht + fr * HLD + 16 * w + 8 * q + 4 * fg) = make_uint2(pk[0], pk[1]);
+    }
+    __syncthreads();
+    bf16_t* Hout = (bf16_t*)outp;
+    const int tid = threadIdx.x, row = tid >> 3, cc = (tid & 7) * 8;
+    const int m = m0 + row, n = ncol0 + cc;   // N % 64 == 0: n < N implies n + 8 <= N
+    if (m < M && n < N)
+      *reinterpret_cast<u32x4*>(Hout + (row_begin + m) * N + n) =
+          *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
+    __syncthreads();   // the next tile's prologue overwrites the LDS
+  } else {
+    float scl[NB];
+    load_scales<NB, GATED, FP8>(a, g, bcol, scl);
+    store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
+  }
 }
 
 // One output tile over K steps [k0, k0 + nk) (the whole K unless split), into outp.
@@ -729,12 +780,15 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
     gemm_bf16_tile<BM_SMALL / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
                                             nk, rot, outp);
   else if (M - mt * BM_SMALL <= SKINNY_ROWS) {
-    if (GATED || !narrow)
-      gemm_bf16_tile_skinny<2, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M, mt * BM_SMALL,
-                                                     ncol0, k0, nk, rot, outp);
-    else if constexpr (!GATED)
-      gemm_bf16_tile_skinny<1, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M, mt * BM_SMALL,
-                                                     ncol0, k0, nk, rot, outp);
+    // (gate/up takes 64-column tiles only when every group fits a skinny tile)
+    if (!narrow)
+      gemm_bf16_tile_skinny<2, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M,
+                                                            mt * BM_SMALL, ncol0, k0, nk, rot,
+                                                            outp);
+    else
+      gemm_bf16_tile_skinny<1, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M,
+                                                            mt * BM_SMALL, ncol0, k0, nk, rot,
+                                                            outp);
   }
   else if (GATED || !narrow)
     gemm_bf16_tile_stream<2, GATED, STREAM_P2, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
@@ -932,6 +986,13 @@ static bool dynamic_tiles(const moe_desc_t& d) {
   return d.T * d.top_k >= (int64_t)SMALL_GROUP_ROWS * d.n_experts;
 }
 
+// Share of the CU slots of the last round left idle by n equal tiles on cus CUs.
+static double idle_fraction(int64_t n, int64_t cus) {
+  if (n <= 0) return 0.0;
+  const int64_t slots = ceil_div(n, cus) * cus;
+  return (double)(slots - n) / (double)slots;
+}
+
 // Upper bound of sum_g ceil(M_g / bm): ceil(T*k / bm) + E (+ ceil(T / bm) shared).
 static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
   return ceil_div(d.T * d.top_k, bm) + d.n_experts + (d.n_shared ? ceil_div(d.T, bm) : 0);
@@ -954,7 +1015,17 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
   a.ksplit = 1;
   a.ctr = dynamic_tiles(d) ? ctr : nullptr;
-  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 128);
+  {
+    // Every group fits a skinny tile (at most T rows each): take 64-column tiles when that
+    // leaves less of the last round idle, e.g. 8 experts x 14336 columns give 896 tiles of
+    // 128 (3.5 rounds of a 256-CU chip) but 1792 of 64 (7 rounds).
+    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, d.T * d.top_k + d.n_shared);
+    const int64_t cus = device_cu_count();
+    a.narrow_small = d.T <= SKINNY_ROWS &&
+                     idle_fraction(groups * ceil_div(d.d_ff, 64), cus) + 0.02 <
+                         idle_fraction(groups * ceil_div(d.d_ff, 128), cus);
+  }
+  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 64);
   if (!bf) return run_f32<true>(a, max_m_tiles(d, 64), s);
   return ew.fp8 ? run_bf16<true, true>(a, mt, s) : run_bf16<true, false>(a, mt, s);
 }
