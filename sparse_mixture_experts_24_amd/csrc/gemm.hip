@@ -694,7 +694,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
   }
   // Steps t >= nk (padding the step count up to a multiple of 3) read zero A rows, so the
   // accumulators are unchanged, and the loop body has no exits.
-#define MOE_STEP(t, cur, nxt2)                                                             \
+#define MOE_STEP_END(t, cur, nxt2)                                                             \
   {                                                                                        \
     MOE_LOAD_A(min((t) + 1, nk - 1));                                                      \
     MOE_LOAD_B(nxt2, (t) + 2);                                                             \
@@ -712,6 +712,68 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
     __syncthreads();                                                                       \
   }
 
+  // Scheduling of a k16 step of the first half: a quarter of the weight loads, then MB x
+  // {NB MFMAs, one fragment read for the second half}.
+#define MOE_SGB_HALF                                                                       \
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * NB, 0);                                  \
+  _Pragma("unroll") for (int j_ = 0; j_ < MB; ++j_) {                                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);                                    \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+  }
+  // K step t (rows in stage t & 1, weights in set cur; the registers ra hold the rows of
+  // step t+1, requested halfway through step t-1).  Halfway through the step, after the
+  // MFMAs of k16 steps 0 and 1, ra goes to the other stage (read last during step t-1,
+  // before the barrier that ended it) and is refilled with the rows of step t+2, so the
+  // LDS writes overlap the MFMAs of k16 steps 2 and 3 instead of stalling the step's end.
+#define MOE_STEP(t, cur, nxt2)                                                             \
+  {                                                                                        \
+    MOE_LOAD_B(nxt2, (t) + 2);                                                             \
+    {                                                                                      \
+      bf16x8 fa[MB], fb[MB];                                                               \
+      MOE_READ_A(fa, (t) & 1, 0);                                                          \
+      MOE_READ_A(fb, (t) & 1, 1);                                                          \
+      MOE_MFMA(fa, cur, 0);                                                                \
+      MOE_READ_A(fa, (t) & 1, 2);                                                          \
+      MOE_MFMA(fb, cur, 1);                                                                \
+      MOE_READ_A(fb, (t) & 1, 3);                                                          \
+      MOE_STORE_A(((t) + 1) & 1);                                                          \
+      MOE_LOAD_A(min((t) + 2, nk - 1));                                                    \
+      MOE_MFMA(fa, cur, 2);                                                                \
+      MOE_MFMA(fb, cur, 3);                                                                \
+    }                                                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);                                \
+    MOE_SGB_HALF                                                                           \
+    MOE_SGB_HALF                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x200, MB, 0);                                    \
+    __builtin_amdgcn_sched_group_barrier(0x020, MB / 2, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);                               \
+    __builtin_amdgcn_sched_group_barrier(0x020, MB - MB / 2, 0);                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    __syncthreads();                                                                       \
+  }
+
+  // Gate/up 256-row tiles store their next rows halfway through each step; the other tiles
+  // (down, and the 128/64-row remainders) store them at the end of the step: the mid-step
+  // order needs more registers live across the step and spills there.
+  if constexpr (GATED && MB == 8) {
+  MOE_LOAD_B(b0, 0);
+  MOE_LOAD_B(b1, 1);
+  MOE_LOAD_A(0);
+  MOE_STORE_A(0);
+  MOE_LOAD_A(min(1, nk - 1));
+  __syncthreads();
+  // Whole triples of steps (the B register sets rotate with period 3), then the last
+  // nk % 3 steps; loads past the last step are clamped to it (in bounds, never used).
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    MOE_STEP(kt, b0, b2);
+    MOE_STEP(kt + 1, b1, b0);
+    MOE_STEP(kt + 2, b2, b1);
+  }
+  if (kt < nk) MOE_STEP(kt, b0, b2);
+  if (kt + 1 < nk) MOE_STEP(kt + 1, b1, b0);
+  } else {
   MOE_LOAD_B(b0, 0);
   MOE_LOAD_B(b1, 1);
   MOE_LOAD_A(0);
@@ -719,9 +781,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
   __syncthreads();
   const int nk3 = (nk + 2) / 3 * 3;
   for (int kt = 0; kt < nk3; kt += 3) {
-    MOE_STEP(kt, b0, b2);
-    MOE_STEP(kt + 1, b1, b0);
-    MOE_STEP(kt + 2, b2, b1);
+    MOE_STEP_END(kt, b0, b2);
+    MOE_STEP_END(kt + 1, b1, b0);
+    MOE_STEP_END(kt + 2, b2, b1);
+  }
   }
 #undef MOE_KSTEP
 #undef MOE_LOAD_B
@@ -729,9 +792,11 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 #undef MOE_STORE_A
 #undef MOE_READ_A
 #undef MOE_MFMA
+#undef MOE_SGB_HALF
+#undef MOE_STEP
 #undef MOE_COMPUTE
 #undef MOE_INTERLEAVE
-#undef MOE_STEP
+#undef MOE_STEP_END
 
   float scl[NB];
   load_scales<NB, GATED, FP8>(a, g, bcol, scl);
