@@ -202,7 +202,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
     roof["kernel"] = ("gemm_bf16_kernel<true, true> (gate/up + SiLU*mul, e4m3 weights)" if fp8
-                      else "gemm_bf16_kernel<true> (gate/up + SiLU*mul)" if wl.dtype == "bf16"
+                      else "gemm_bf16_kernel<true, false> (gate/up + SiLU*mul)" if wl.dtype == "bf16"
                       else "gemm_f32_kernel<true>")
     roof["kernel_ms"] = stage_ms["gate_up"]
     roof["algorithmic_per_launch"] = flops_gate_up if bound != "hbm" else bytes_gate_up
@@ -296,13 +296,16 @@ def summarize_pmc(workload, fetch_csv, write_csv):
             raise SystemExit(f"no matching kernel among {sorted(d)}")
         return statistics.median([v for k in names for v in d[k]])
 
-    is_gemm = lambda k: "gemm_bf16_kernel<true>" in k or "gemm_bf16_kernelILb1E" in k
+    import gen
+    gemm_name = "gemm_bf16_kernel<true, %s>" % ("true" if gen.workload(workload).weights == "fp8"
+                                                 else "false")
+    is_gemm = lambda k: gemm_name in k
     is_copy = lambda k: "MulFunctor" in k
     f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     gf, gw = pick(f, is_gemm), pick(w, is_gemm)
     cf, cw = pick(f, is_copy), pick(w, is_copy)
     sf, sw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
-    rec = {"workload": workload, "kernel": "gemm_bf16_kernel<true> (gate/up + SiLU*mul)",
+    rec = {"workload": workload, "kernel": gemm_name + " (gate/up + SiLU*mul)",
            "source_sha256": gemm_source_hash(),
            "fetch_kib_per_launch": gf, "write_kib_per_launch": gw,
            "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf, "copy_write_kib": cw,
