@@ -12,7 +12,8 @@
 // 32 contiguous bytes of a row per 64-wide k chunk (a row's 128 bytes come from 4
 // lanes), and the two MFMAs of the chunk take the first and second 16 bytes: A and B
 // use the same k mapping, so the sum is over the same pairs as a plain dot product.
-// The top-k runs one wavefront per token with shuffle reductions.
+// The top-k runs one wavefront per token; its reductions move data between lanes with DPP
+// and v_permlane16/32_swap (no LDS round trips).
 #include <math.h>
 
 #include "moe_internal.h"
@@ -22,13 +23,78 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// Lane exchanges for wave-wide reductions.  Inside a 16-lane row: DPP quad swaps (1,0,3,2)
+// and (2,3,0,1), then the half-row and row mirrors; across rows: v_permlane16_swap and
+// v_permlane32_swap, which hand every lane the values of both rows (or halves) of its pair.
+// After each step every lane of the group holds op(a, b) of the same two values, so with a
+// commutative op all 64 lanes end with the same bits.
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_HALF_MIRROR = 0x141,
+              DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+template <class Op>
+__device__ inline float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f<DPP_QUAD_1032>(v));
+  v = op(v, dpp_f<DPP_QUAD_2301>(v));
+  v = op(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = op(v, dpp_f<DPP_MIRROR>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return op(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 __device__ inline float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ inline float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+
+// (v, e) <- the better of (v, e) and (ov, oe): larger score, lower expert on equal scores.
+__device__ inline void take_better(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+template <int CTRL>
+__device__ inline void argmax_step(float& v, int& e) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oe = dpp_i<CTRL>(e);
+  take_better(v, e, ov, oe);
+}
+// Wave-wide argmax of (score, expert); every lane ends with the winner.
+__device__ inline void wave_argmax(float& v, int& e) {
+  argmax_step<DPP_QUAD_1032>(v, e);
+  argmax_step<DPP_QUAD_2301>(v, e);
+  argmax_step<DPP_HALF_MIRROR>(v, e);
+  argmax_step<DPP_MIRROR>(v, e);
+  {
+    const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+    const auto re = __builtin_amdgcn_permlane16_swap((unsigned)e, (unsigned)e, false, false);
+    v = __uint_as_float(rv[0]);
+    e = (int)re[0];
+    take_better(v, e, __uint_as_float(rv[1]), (int)re[1]);
+  }
+  {
+    const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+    const auto re = __builtin_amdgcn_permlane32_swap((unsigned)e, (unsigned)e, false, false);
+    v = __uint_as_float(rv[0]);
+    e = (int)re[0];
+    take_better(v, e, __uint_as_float(rv[1]), (int)re[1]);
+  }
 }
 
 // Softmax + top-k + renorm for the tokens of one block, logits in LDS rows of E_PAD.
@@ -79,7 +145,7 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
     }
     unsigned taken = 0;
     int my_idx = 0;
-    float my_p = 0.0f, s_k = 0.0f;
+    float my_p = 0.0f, s_k = 0.0f, tot = 0.0f;
     // k rounds of wavefront argmax (one more, not taken, when the gap is asked for)
     const int rounds = k + (gap != nullptr ? 1 : 0);
     for (int r = 0; r < rounds; ++r) {
@@ -93,14 +159,7 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
           be = e;
         }
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bvv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        if (ov > bvv || (ov == bvv && oe < be)) {
-          bvv = ov;
-          be = oe;
-        }
-      }
+      wave_argmax(bvv, be);
       if (r == k) {            // gap = s_(k) - s_(k+1); +inf when k == E
         if (lane == 0) gap[t] = s_k - bvv;
         break;
@@ -113,15 +172,14 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
       for (int i = 0; i < NV; ++i)
         if (i == slot) pp = v[i];
       if (ok && lane == owner) taken |= 1u << slot;
-      pp = __shfl(pp, owner, 64);
+      pp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), owner));
+      tot += pp;   // sum of the chosen p in slot order
       if (lane == r) {
         my_idx = be;
         my_p = pp;
       }
       if (lane == 0 && be < E) atomicAdd(&cnt[be], 1);
     }
-    float tot = 0.0f;
-    for (int r = 0; r < k; ++r) tot += __shfl(my_p, r, 64);
     if (lane < k) {
       topk_idx[(size_t)t * k + lane] = my_idx;
       topk_w[(size_t)t * k + lane] = my_p / tot;
@@ -146,7 +204,7 @@ __device__ inline void route_block_stats(const float* psum, float (*pw)[E_PAD], 
   }
 }
 
-template <int EPW, int TPW, int KS, int U>
+template <int EPW, int TPW, int KS, int R>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -171,12 +229,11 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     const int t = min(t0 + tb * 16 + r, T - 1);
     arow[tb] = x + (size_t)t * d + g * 16;
   }
+  // Expert rows past E (padding of the last slab) read row E-1; their logits are never used.
   const bf16_t* brow[EPW];
-  bool bok[EPW];
 #pragma unroll
   for (int eb = 0; eb < EPW; ++eb) {
     const int e = (ew * EPW + eb) * 16 + r;
-    bok[eb] = e < E;
     brow[eb] = Wr + (size_t)min(e, E - 1) * d + g * 16;
   }
   floatx4 acc[TPW][EPW];
@@ -185,49 +242,51 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 #pragma unroll
     for (int eb = 0; eb < EPW; ++eb) acc[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // This wave's 64-wide k chunks are c = ks + KS*j, j < nj.  They are processed in
-  // batches of U chunks with two register buffers: the loads of batch b+1 are in flight
-  // while the MFMAs of batch b run.  Chunks past the end load a valid address and a zero
-  // B fragment, so the batch loop needs no exits.
+  // This wave's 64-wide k chunks are c = ks + KS*j, j < nj.  Their fragments go through a
+  // ring of R register slots, loaded R-1 chunks ahead of the MFMAs.  Whole passes over
+  // the ring run unguarded (a load past the end reads the last chunk again, a valid
+  // address, and is never used); the remaining chunks, already loaded, finish after the
+  // loop.  No loaded value is touched before its chunk's turn, so the loads of the next
+  // R-1 chunks stay in flight while a chunk's MFMAs run.
   const int nchunk = d / 64;
   const int nj = (nchunk - ks + KS - 1) / KS;
-  const int nbatch = (nj + U - 1) / U;
-  bf16x8 xa[2][U][TPW][2], xb[2][U][EPW][2];
-#define R_LOAD(BUF, batch)                                                                  \
-  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                           \
-    const int j_ = (batch) * U + u;                                                         \
-    const bool live_ = j_ < nj;                                                             \
-    const int c_ = ks + KS * min(j_, nj - 1);                                               \
+  bf16x8 xa[R][TPW][2], xb[R][EPW][2];
+#define R_LOAD(SLOT, j)                                                                     \
+  {                                                                                         \
+    const int c_ = ks + KS * min((j), nj - 1);                                              \
     _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb) {                                    \
       const bf16x8* pa = reinterpret_cast<const bf16x8*>(arow[tb] + c_ * 64);               \
-      xa[BUF][u][tb][0] = pa[0];                                                            \
-      xa[BUF][u][tb][1] = pa[1];                                                            \
+      xa[SLOT][tb][0] = pa[0];                                                              \
+      xa[SLOT][tb][1] = pa[1];                                                              \
     }                                                                                       \
     _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb) {                                    \
       const bf16x8* pb = reinterpret_cast<const bf16x8*>(brow[eb] + c_ * 64);               \
-      xb[BUF][u][eb][0] = pb[0];                                                            \
-      xb[BUF][u][eb][1] = pb[1];                                                            \
-      if (!(bok[eb] && live_)) {                                                            \
-        xb[BUF][u][eb][0] = bf16x8{};                                                       \
-        xb[BUF][u][eb][1] = bf16x8{};                                                       \
-      }                                                                                     \
+      xb[SLOT][eb][0] = pb[0];                                                              \
+      xb[SLOT][eb][1] = pb[1];                                                              \
     }                                                                                       \
   }
-#define R_MFMA(BUF)                                                                         \
-  _Pragma("unroll") for (int u = 0; u < U; ++u)                                             \
-    _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                      \
-      _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                    \
-        _Pragma("unroll") for (int h = 0; h < 2; ++h)                                       \
-          acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                            \
-              xa[BUF][u][tb][h], xb[BUF][u][eb][h], acc[tb][eb], 0, 0, 0);
+#define R_MFMA(SLOT)                                                                        \
+  _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                        \
+    _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                      \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                         \
+        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+            xa[SLOT][tb][h], xb[SLOT][eb][h], acc[tb][eb], 0, 0, 0);
   if (nj > 0) {
-    R_LOAD(0, 0);
-    for (int b = 0; b < nbatch; b += 2) {
-      R_LOAD(1, b + 1);
-      R_MFMA(0);
-      R_LOAD(0, b + 2);
-      R_MFMA(1);
+#pragma unroll
+    for (int q = 0; q < R - 1; ++q) R_LOAD(q, q);
+    int j0 = 0;
+    for (; j0 + R <= nj; j0 += R) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        R_LOAD((q + R - 1) % R, j0 + q + R - 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep each load group ahead of the MFMAs
+        R_MFMA(q);
+      }
     }
+    // The last nj - j0 < R chunks are already in slots 0 .. nj - j0 - 1.
+#pragma unroll
+    for (int q = 0; q < R - 1; ++q)
+      if (j0 + q < nj) R_MFMA(q);
   }
 #undef R_LOAD
 #undef R_MFMA
@@ -353,11 +412,12 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   }
   const bf16_t* xx = (const bf16_t*)x;
   const bf16_t* ww = (const bf16_t*)W_router;
-// U: k chunks per batch, as many as two register buffers of fragments allow.
+// R: ring slots of k-chunk fragments (8 (EPW + TPW) VGPRs each, about 200 VGPRs in all),
+// at most 8, so the loads in flight (2 (EPW + TPW) per slot) stay within what vmcnt counts.
 #define MOE_ROUTE_BF16(EPW_, TPW_, KS_)                                                      \
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
-    constexpr int U_ = (EPW_ + TPW_) <= 2 ? 4 : ((EPW_ + TPW_) <= 4 ? 2 : 1);                 \
-    hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, U_>), grid, block, 0, s, xx, ww,   \
+    constexpr int R_ = (EPW_ + TPW_) <= 3 ? 8 : 200 / (8 * (EPW_ + TPW_));                      \
+    hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, R_>), grid, block, 0, s, xx, ww,   \
                        bias, T, dm, E, k, topk_idx, topk_w, gap, p_part, cnt_part);           \
     return hipGetLastError();                                                                 \
   }
