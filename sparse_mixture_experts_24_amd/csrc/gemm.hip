@@ -169,12 +169,12 @@ constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 // every CU must take part).
 __device__ inline bool small_group(int M) { return M < SMALL_GROUP_ROWS; }
 // Rows of m-tile mt (tiles start at mt * 256 in large groups, mt * 64 in small ones):
-// large groups take 256-row tiles and put their remainder in one tile of 64, 128 or 256
-// rows, whichever is the smallest that holds it.
+// large groups take 256-row tiles and put their remainder in one tile of 64, 128, 192 or
+// 256 rows, whichever is the smallest that holds it.
 __device__ inline int m_tile_rows(int M, int mt) {
   if (small_group(M)) return BM_SMALL;
   const int r = M - mt * BM_BIG;
-  return r >= BM_BIG ? BM_BIG : (r <= 64 ? 64 : (r <= 128 ? 128 : BM_BIG));
+  return r > 192 ? BM_BIG : r > 128 ? 192 : r > 64 ? 128 : 64;
 }
 template <bool GATED>
 __device__ inline int tile_cols(bool small, int narrow_small) {
@@ -838,6 +838,9 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   if (!sm && rows == BM_BIG)
     gemm_bf16_tile<BM_BIG / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
                                           rot, outp);
+  else if (!sm && rows == 192)
+    gemm_bf16_tile<192 / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
+                                       rot, outp);
   else if (!sm && rows == 128)
     gemm_bf16_tile<128 / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
                                        rot, outp);
