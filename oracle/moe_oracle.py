@@ -35,7 +35,12 @@ notes of the repository):
     [MoE practice], section on quantisation and routing, keeps the router in high
     precision while the expert weights take the quantisation) are e4m3 "fn" codes with
     one float32 scale per output row, dequantised exactly before the same arithmetic;
-    the router, x and h stay as in the bf16 layer.
+    the router, x and h stay as in the bf16 layer;
+  * expert-choice routing (the second routing of the pages: [MoE memo] routing-design
+    table, [MoE practice] top-k section) scores tokens by the softmax probabilities,
+    gives each expert the C = min(T, max(floor(cf * k * T / E), k)) tokens with the
+    largest score (ties to the lower token index), and weights each output by that
+    probability without renormalisation.
 
 Pins: tests/test_oracle_pins.py checks each function against values the pages print,
 closed forms, library routines and brute force.  Large-shape absolute values are
@@ -344,3 +349,90 @@ def forward_rows(inputs: dict, rows, k: int, capacity_factor: float = 0.0,
     if n_shared:
         y += expert_ffn(x[rows], *expert_weights(inputs, E), h_bf16).astype(F64)
     return y.astype(F32)
+
+
+# ----------------------------------------------------------------------------- expert choice
+def expert_choice_capacity(T: int, k: int, E: int, cf: float) -> int:
+    """Tokens each expert takes under expert-choice routing: the per-expert capacity of
+    ``capacity`` (C = max(floor(cf * k * T / E), k), k read as the average number of
+    experts per token), at most T.  cf must be > 0.
+
+    [MoE practice] top-k section: each expert takes its top-C tokens according to its
+    capacity; the capacity is the routing-math section's.
+    """
+    if cf is None or cf <= 0:
+        raise ValueError("expert-choice routing needs a capacity factor > 0")
+    return min(T, capacity(T, k, E, cf))
+
+
+def expert_choice_select(p: np.ndarray, C: int):
+    """Each expert takes the C tokens with the largest router probability p[t, e].
+
+    [MoE memo] routing section (the expert-choice row of the routing-design table: each
+    expert picks the tokens that suit it, so every expert's load is equal); [MoE
+    practice] top-k section (each expert picks its top-C tokens).  The scores are the
+    token-wise softmax probabilities of ``router_probs`` (no bias), compared in float32;
+    equal scores go to the lower token index.
+
+    Returns (sel [E, C] int32: expert e's tokens in ascending token order, margin [E]
+    float64: the gap between the C-th and the (C+1)-th largest p of the column, +inf when
+    C == T; a column with margin < 1e-6 may be chosen either way in float32).
+    """
+    T, E = p.shape
+    sel = np.empty((E, C), np.int32)
+    margin = np.full(E, np.inf)
+    for e in range(E):
+        col = p[:, e].astype(F32).astype(F64)
+        order = np.argsort(-col, kind="stable")    # stable: lower token first on ties
+        sel[e] = np.sort(order[:C])
+        if C < T:
+            margin[e] = col[order[C - 1]] - col[order[C]]
+    return sel, margin
+
+
+def expert_choice_dispatch(sel: np.ndarray, T: int) -> dict:
+    """Rows and slots of an expert-choice selection: expert e's rows are
+    [e*C, (e+1)*C), holding its tokens in ascending order; slot[t, e] is the row of
+    (t, e) or -1 when expert e did not take token t."""
+    E, C = sel.shape
+    offsets = (np.arange(E + 1, dtype=np.int64) * C).astype(np.int32)
+    perm_src = sel.reshape(-1).astype(np.int32)
+    slot = np.full((T, E), -1, np.int32)
+    for e in range(E):
+        slot[sel[e], e] = e * C + np.arange(C, dtype=np.int32)
+    return {"offsets": offsets, "perm_src": perm_src, "slot": slot}
+
+
+def forward_expert_choice(inputs: dict, k: int, capacity_factor: float, n_shared: int = 0,
+                          h_bf16: bool = True, sel_override=None) -> dict:
+    """The layer with expert-choice routing.
+
+    p = router_probs(x, W_router); each expert takes its top-C tokens
+    (``expert_choice_select``); every expert runs the SwiGLU FFN on its C tokens;
+    y[t] = sum over the experts e that took t, in ascending e, of p[t, e] * o_e(t), plus
+    the shared expert with weight 1.  The weights are the probabilities themselves (the
+    pages give no renormalisation for this routing); a token no expert took outputs 0
+    (+ shared).  P_e = mean_t p[t, e] as for token choice; f_e = share of the E*C
+    assignments, 1/E.  ``sel_override`` replaces the selection (near-tied columns).
+    """
+    x = _np(inputs["x"])
+    Wr = _np(inputs["W_router"])
+    T, d = x.shape
+    E = Wr.shape[0]
+    p = router_probs(x, Wr)
+    C = expert_choice_capacity(T, k, E, capacity_factor)
+    sel, margin = expert_choice_select(p, C)
+    if sel_override is not None:
+        sel = np.asarray(sel_override, np.int32)
+    disp = expert_choice_dispatch(sel, T)
+    Y = np.zeros((E * C, d), F32)
+    for e in range(E):
+        if C:
+            Y[e * C:(e + 1) * C] = expert_ffn(x[sel[e]], *expert_weights(inputs, e), h_bf16)
+    shared = expert_ffn(x, *expert_weights(inputs, E), h_bf16) if n_shared else None
+    y = combine(T, d, p, disp["slot"].reshape(-1), Y, shared)
+    counts = np.full(E, C, np.int64)
+    f = (counts.astype(F64) / float(max(E * C, 1))).astype(F32)
+    P = p.astype(F64).mean(axis=0).astype(F32)
+    return {"y": y, "f": f, "p": P, "probs": p, "sel": sel, "margin": margin, "C": C,
+            "dispatch": disp}

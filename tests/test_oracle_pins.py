@@ -475,3 +475,156 @@ def test_fp8_planted_mistakes_are_caught(monkeypatch):
                   lambda q, s: np.resize(np.asarray(s, np.float64), q.shape[1])[None, :]
                   * orig(q))
         assert _pins_fail(test_fp8_expert_weights_are_scale_times_code)
+
+
+# --------------------------------------------------------------------------- expert choice
+def brute_expert_choice(p, C):
+    """Python-sorted selection: per expert, tokens ordered by (-p, t), first C, ascending."""
+    T, E = p.shape
+    out = []
+    for e in range(E):
+        ranked = sorted(range(T), key=lambda t: (-float(p[t, e]), t))
+        out.append(sorted(ranked[:C]))
+    return np.array(out, np.int32).reshape(E, C)
+
+
+def test_expert_choice_hand_example():
+    """4 tokens, 2 experts, C = 2: expert 0 takes token 0 and the lower of the tied
+    tokens 1 and 2; expert 1 takes token 3 and again token 1; nobody takes token 2."""
+    p = np.array([[0.9, 0.1], [0.5, 0.5], [0.5, 0.5], [0.1, 0.9]], np.float32)
+    sel, margin = oracle.expert_choice_select(p, 2)
+    assert sel.tolist() == [[0, 1], [1, 3]]
+    assert margin.tolist() == [0.0, 0.0]
+    disp = oracle.expert_choice_dispatch(sel, 4)
+    assert disp["slot"].tolist() == [[0, -1], [1, 2], [-1, -1], [-1, 3]]
+    assert disp["offsets"].tolist() == [0, 2, 4]
+
+
+@pytest.mark.parametrize("T,E,C,seed", [(12, 3, 4, 0), (40, 8, 7, 1), (9, 5, 9, 2), (33, 4, 1, 3)])
+def test_expert_choice_select_brute_force(T, E, C, seed):
+    rng = np.random.default_rng(seed)
+    # coarse values so that ties occur
+    p = (rng.integers(0, 6, (T, E)) / 8.0).astype(np.float32)
+    sel, margin = oracle.expert_choice_select(p, C)
+    np.testing.assert_array_equal(sel, brute_expert_choice(p, C))
+    for e in range(E):
+        col = np.sort(p[:, e].astype(np.float64))[::-1]
+        assert margin[e] == (np.inf if C == T else col[C - 1] - col[C])
+
+
+def test_expert_choice_capacity():
+    assert oracle.expert_choice_capacity(4096, 2, 8, 1.0) == 1024
+    assert oracle.expert_choice_capacity(10, 2, 8, 1.0) == 2          # at least k
+    assert oracle.expert_choice_capacity(10, 2, 8, 100.0) == 10       # at most T
+    with pytest.raises(ValueError):
+        oracle.expert_choice_capacity(10, 2, 8, 0.0)
+
+
+def per_token_expert_choice(inp, k, cf, S, h_bf16):
+    """Independent formulation: the selection by Python sorting, then one token at a
+    time over the experts that took it."""
+    x = inp["x"].astype(np.float64)
+    T, d = x.shape
+    E = inp["W_router"].shape[0]
+    C = min(T, max(int(math.floor(cf * k * T / E)), k))
+    logits = x @ inp["W_router"].astype(np.float64).T
+    ex = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    taken = [set(s) for s in brute_expert_choice(p, C).tolist()]
+    y = np.zeros((T, d))
+    for t in range(T):
+        for e in range(E + S):
+            if e < E and t not in taken[e]:
+                continue
+            g = inp["W_gate"][e].astype(np.float64) @ x[t]
+            u = inp["W_up"][e].astype(np.float64) @ x[t]
+            h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+            if h_bf16:
+                h = oracle.bf16_round(h)
+            o = (inp["W_down"][e].astype(np.float64) @ h.astype(np.float64)).astype(np.float32)
+            y[t] += (float(p[t, e]) if e < E else 1.0) * o.astype(np.float64)
+    return y.astype(np.float32)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,S,cf,hb", [
+    (24, 16, 6, 2, 20, 0, 1.0, False),
+    (30, 12, 5, 1, 8, 1, 1.25, True),
+    (17, 8, 4, 3, 12, 0, 0.5, True),
+])
+def test_expert_choice_forward_matches_per_token_loop(T, d, E, k, F, S, cf, hb):
+    inp = make_small(T, d, E, k, F, S, seed=3 * T + d)
+    out = oracle.forward_expert_choice(inp, k, cf, S, h_bf16=hb)
+    ref = per_token_expert_choice(inp, k, cf, S, hb)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-5, atol=1e-6)
+    C = out["C"]
+    assert out["sel"].shape == (E, C)
+    np.testing.assert_allclose(out["f"], np.full(E, 1.0 / E), rtol=1e-6)
+    np.testing.assert_allclose(out["p"], oracle.router_probs(inp["x"], inp["W_router"]).mean(0),
+                               rtol=1e-6)
+
+
+def test_expert_choice_every_token_reduces_to_dense_mixture():
+    """With C = T every expert takes every token, so y_t = sum_e p[t, e] FFN_e(x_t); with
+    identical experts the probabilities sum to one and y is the dense FFN."""
+    T, d, E, F = 20, 16, 5, 24
+    inp = make_small(T, d, E, 1, F, seed=5)
+    out = oracle.forward_expert_choice(inp, E, 1.0, 0, h_bf16=False)   # C = T
+    assert out["C"] == T
+    p = oracle.router_probs(inp["x"], inp["W_router"]).astype(np.float64)
+    mix = sum(p[:, e:e + 1] * oracle.expert_ffn(inp["x"], inp["W_gate"][e], inp["W_up"][e],
+                                                inp["W_down"][e], False).astype(np.float64)
+              for e in range(E))
+    np.testing.assert_allclose(out["y"], mix, rtol=1e-5, atol=1e-6)
+    for key in ("W_gate", "W_up", "W_down"):
+        inp[key] = np.repeat(inp[key][:1], E, axis=0)
+    dense = oracle.expert_ffn(inp["x"], inp["W_gate"][0], inp["W_up"][0], inp["W_down"][0], False)
+    y = oracle.forward_expert_choice(inp, E, 1.0, 0, h_bf16=False)["y"]
+    np.testing.assert_allclose(y, dense, rtol=2e-6, atol=1e-6)
+
+
+def test_expert_choice_loads_are_equal_and_untaken_tokens_give_zero():
+    T, d, E, F = 64, 8, 4, 8
+    inp = make_small(T, d, E, 1, F, seed=9)
+    out = oracle.forward_expert_choice(inp, 1, 0.25, 0, h_bf16=False)   # C = 4 of 64
+    C = out["C"]
+    assert C == 4
+    slot = out["dispatch"]["slot"]
+    assert ((slot >= 0).sum(axis=0) == C).all()
+    untaken = np.nonzero((slot < 0).all(axis=1))[0]
+    assert untaken.size >= T - E * C
+    assert not out["y"][untaken].any()
+
+
+def test_expert_choice_planted_mistakes_are_caught(monkeypatch):
+    """Ties to the higher token index, the lowest instead of the highest scores, tokens
+    ranked by logits instead of probabilities, or renormalised weights fail a pin."""
+    with monkeypatch.context() as m:
+        m.setattr(mo, "expert_choice_select",
+                  lambda p, C: (np.sort(np.array([np.argsort(-p[:, e].astype(np.float64)[::-1],
+                                                              kind="stable")[:C] * -1 + p.shape[0] - 1
+                                                  for e in range(p.shape[1])]), axis=1)
+                                .astype(np.int32), np.zeros(p.shape[1])))
+        m.setattr(oracle, "expert_choice_select", mo.expert_choice_select)
+        assert _pins_fail(test_expert_choice_hand_example)
+    with monkeypatch.context() as m:
+        m.setattr(mo, "expert_choice_select",
+                  lambda p, C: (np.sort(np.argsort(p.T.astype(np.float64), axis=1,
+                                                   kind="stable")[:, :C], axis=1).astype(np.int32),
+                                np.zeros(p.shape[1])))
+        m.setattr(oracle, "expert_choice_select", mo.expert_choice_select)
+        assert _pins_fail(lambda: test_expert_choice_select_brute_force(40, 8, 7, 1))
+    orig_probs = mo.router_probs
+    with monkeypatch.context() as m:
+        m.setattr(mo, "router_probs",
+                  lambda x, W: (x.astype(np.float64) @ W.astype(np.float64).T).astype(np.float32))
+        assert _pins_fail(lambda: test_expert_choice_forward_matches_per_token_loop(
+            24, 16, 6, 2, 20, 0, 1.0, False))
+    orig_combine = mo.combine
+    with monkeypatch.context() as m:
+        m.setattr(mo, "combine",
+                  lambda T, d, w, sp, Y, sh=None: orig_combine(
+                      T, d, (w / np.maximum(np.where(sp.reshape(w.shape) >= 0, w, 0).sum(1,
+                             keepdims=True), 1e-30)).astype(np.float32), sp, Y, sh))
+        assert _pins_fail(lambda: test_expert_choice_forward_matches_per_token_loop(
+            24, 16, 6, 2, 20, 0, 1.0, False))
+    assert orig_probs is mo.router_probs
