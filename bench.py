@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 # Which roof bounds the dominant (gate/up) kernel for each workload.
 BOUND = {"mixtral_prefill": "mfma", "fine_grained_shared": "mfma", "mixtral_decode": "hbm",
          "switch_capacity": "hbm", "tiny_f32": "alu", "mixtral_decode_fp8": "hbm",
-         "switch_capacity_fp8": "hbm"}
+         "switch_capacity_fp8": "hbm", "mixtral_prefill_ec": "mfma"}
 
 
 def log(*a):
@@ -75,9 +75,10 @@ def main():
 
     T, d, E, k, F, S = wl.T, wl.d, wl.E, wl.k, wl.F, wl.n_shared
     fp8 = wl.weights == "fp8"     # e4m3 expert weights with per-row scales
+    ec = wl.routing == "expert"   # expert-choice routing: each expert takes its top-C tokens
     out_dtype = wl.torch_dtype
     desc = moe.make_desc(T, d, E, F, k, S, wl.capacity_factor, wl.torch_dtype, out_dtype)
-    ws = moe.alloc_workspace(desc, dev)
+    ws = moe.alloc_workspace_expert_choice(desc, dev) if ec else moe.alloc_workspace(desc, dev)
     out = torch.empty(T, d, dtype=out_dtype, device=dev)
     f = torch.empty(E, dtype=torch.float32, device=dev)
     p = torch.empty(E, dtype=torch.float32, device=dev)
@@ -86,7 +87,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     dref = ctypes.byref(desc)
-    if fp8:
+    if ec:
+        fwd_fn = L.moe_forward_expert_choice
+        fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["W_gate"]),
+                    P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p), P(ws), ws.numel(), sp)
+    elif fp8:
         W8 = [P(dinp[n]) for n in ("Wq_gate", "Wq_up", "Wq_down", "s_gate", "s_up", "s_down")]
         fwd_fn = L.moe_forward_fp8
         fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]), *W8,
@@ -124,9 +129,9 @@ def main():
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     slot = torch.empty(T * k, dtype=torch.int32, device=dev)
     rows = T * k + S * T
+    out2 = torch.empty_like(out)
     H = torch.empty(rows, F, dtype=wl.torch_dtype, device=dev)
     Yp = torch.empty(rows, d, dtype=torch.float32, device=dev)
-    out2 = torch.empty_like(out)
     calls = [
         ("route", lambda: L.moe_route(dref, P(dinp["x"]), P(dinp["W_router"]),
                                       P(dinp["router_bias"]), P(idx), P(w), None, P(f), P(p), P(ws),
@@ -146,6 +151,9 @@ def main():
                                      ws.numel(), sp))),
         ("combine", lambda: L.moe_combine(dref, P(Yp), P(slot), P(w), P(out2), sp)),
     ]
+    if ec:   # the expert-choice layer's own stages
+        calls = expert_choice_stages(moe, L, desc, dinp, ws, out2, f, p, P, sp, dev)
+        counts, offsets = calls.counts, calls.offsets
     for _ in range(max(1, args.warmup)):
         for name, c in calls:
             if c():
@@ -220,7 +228,7 @@ def main():
     # ---- CPU oracle on a bounded sample of the same batch
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, args.cpu_sample)
+        cpu = (cpu_baseline_ec if ec else cpu_baseline)(wl, inp, args.cpu_sample)
 
     rec = {
         "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
@@ -230,7 +238,9 @@ def main():
         "config": {"workload": wl.name, "T": T, "d_model": d, "n_experts": E, "top_k": k,
                    "d_ff": F, "n_shared": S, "capacity_factor": wl.capacity_factor,
                    "selection_bias": wl.bias_range > 0, "out_dtype": str(out_dtype).split(".")[-1],
-                   "expert_weights": "e4m3 + f32 per-row scale" if fp8 else wl.dtype},
+                   "expert_weights": "e4m3 + f32 per-row scale" if fp8 else wl.dtype,
+                   "routing": "expert choice (top-C tokens per expert)" if ec
+                              else "token choice (top-k experts per token)"},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,
@@ -350,6 +360,91 @@ def cpu_baseline(wl, inp, sample):
     return {"value": wl.T / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"routing+dispatch of all {wl.T} tokens ({t_route:.2f}s) + experts of "
                       f"{rows.size} evenly spaced tokens ({t_exp:.2f}s), scaled to the batch"}
+
+
+class _Stages(list):
+    """(name, call) pairs plus the buffers the bench reads back afterwards."""
+
+
+def expert_choice_stages(moe, L, desc, dinp, ws, out2, f, p, P, sp, dev):
+    """The expert-choice layer's kernels through its stage entry points: route +
+    selection, gate/up, down, combine.  The two GEMMs are the same launches as inside
+    moe_forward_expert_choice, reached through the token-choice stage entry points with
+    one row per routed (token, expert) pair: a description with T' = E*C tokens and k = 1,
+    and x padded to E*C rows (the rows read are perm_src's, all below T)."""
+    import torch
+    T, d, E, F, k, S = desc.T, desc.d_model, desc.n_experts, desc.d_ff, desc.top_k, desc.n_shared
+    if S:
+        raise SystemExit("expert-choice stage timing covers layers without a shared expert")
+    dt = dinp["x"].dtype
+    C = moe.capacity_expert_choice(desc)
+    probs = torch.empty(T, E, dtype=torch.float32, device=dev)
+    slot = torch.empty(T, E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(E * C, dtype=torch.int32, device=dev)
+    xpad = torch.zeros(E * C, d, dtype=dt, device=dev)
+    xpad[:T] = dinp["x"]
+    dpad = moe.make_desc(E * C, d, E, F, 1, 0, 0.0, dt, dt)
+    wpad = moe.alloc_workspace(dpad, dev)
+    H = torch.empty(E * C, F, dtype=dt, device=dev)
+    Yp = torch.empty(E * C, d, dtype=torch.float32, device=dev)
+    dref, pref = ctypes.byref(desc), ctypes.byref(dpad)
+    st = _Stages([
+        ("route", lambda: L.moe_route_expert_choice(
+            dref, P(dinp["x"]), P(dinp["W_router"]), P(probs), P(offsets), P(perm), P(slot),
+            P(f), P(p), P(ws), ws.numel(), sp)),
+        ("gate_up", lambda: L.moe_experts_gate_up(pref, P(xpad), P(perm), P(offsets),
+                                                  P(dinp["W_gate"]), P(dinp["W_up"]), P(H),
+                                                  P(wpad), wpad.numel(), sp)),
+        ("down", lambda: L.moe_experts_down(pref, P(H), P(offsets), P(dinp["W_down"]), P(Yp),
+                                            P(wpad), wpad.numel(), sp)),
+        ("combine", lambda: L.moe_combine_expert_choice(dref, P(Yp), P(slot), P(probs),
+                                                        P(out2), sp)),
+    ])
+    st.counts = torch.full((E,), C, dtype=torch.int32, device=dev)
+    st.offsets = offsets
+    return st
+
+
+def cpu_baseline_ec(wl, inp, sample):
+    """The oracle on the host for an expert-choice layer: probabilities and the per-expert
+    selection of the whole batch, plus the experts of a sample of tokens (each through
+    every expert that took it), scaled to the whole batch."""
+    import numpy as np
+
+    import oracle
+    from oracle import moe_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    if not sample:
+        per_tok = 6.0 * wl.d * wl.F * (wl.k + wl.n_shared)
+        sample = int(max(8, min(wl.T, 6.0e12 / per_tok)))
+    t0 = time.perf_counter()
+    x = mo._np(inp["x"])
+    probs = oracle.router_probs(x, mo._np(inp["W_router"]))
+    C = oracle.expert_choice_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    sel, _ = oracle.expert_choice_select(probs, C)
+    t_route = time.perf_counter() - t0
+    rows = np.linspace(0, wl.T - 1, sample).astype(np.int64)
+    t1 = time.perf_counter()
+    hb = wl.dtype == "bf16"
+    y = np.zeros((rows.size, wl.d))
+    for e in range(wl.E):
+        hit = np.nonzero(np.isin(rows, sel[e]))[0]
+        if hit.size:
+            o = oracle.expert_ffn(x[rows[hit]], *oracle.expert_weights(inp, e), hb)
+            y[hit] += probs[rows[hit], e].astype(np.float64)[:, None] * o
+    t_exp = time.perf_counter() - t1
+    full = t_route + t_exp * wl.T / rows.size
+    log(f"[bench] oracle: probabilities+selection {t_route:.2f}s for {wl.T} tokens, experts "
+        f"{t_exp:.2f}s for {rows.size} tokens -> {full:.1f}s per batch")
+    return {"value": wl.T / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"probabilities and expert-choice selection of all {wl.T} tokens "
+                      f"({t_route:.2f}s) + experts of {rows.size} evenly spaced tokens "
+                      f"({t_exp:.2f}s), scaled to the batch"}
 
 
 if __name__ == "__main__":

@@ -53,6 +53,7 @@ class Workload:
     bias_range: float = 0.0           # > 0: selection bias ~ U(-r, r)
     row_scales: tuple | None = None   # per-expert router row scale (load skew)
     weights: str = "same"             # "same" (as dtype) or "fp8": e4m3 expert weights
+    routing: str = "token"            # "token" (top-k per token) or "expert" (top-C per expert)
     recipe: str = ""
 
     def replace(self, **kw) -> "Workload":
@@ -98,6 +99,12 @@ WORKLOADS["mixtral_decode_fp8"] = WORKLOADS["mixtral_decode"].replace(
 WORKLOADS["switch_capacity_fp8"] = WORKLOADS["switch_capacity"].replace(
     name="switch_capacity_fp8", weights="fp8",
     recipe=WORKLOADS["switch_capacity"].recipe + "; expert weights e4m3 with per-row scales")
+# The prefill layer's inputs (same seeds, same values) under expert-choice routing: each
+# expert takes C = T k / E = 1024 tokens.
+WORKLOADS["mixtral_prefill_ec"] = WORKLOADS["mixtral_prefill"].replace(
+    name="mixtral_prefill_ec", capacity_factor=1.0, routing="expert",
+    recipe=WORKLOADS["mixtral_prefill"].recipe + "; expert-choice routing, capacity factor 1 "
+    "(C = 1024 tokens per expert)")
 
 
 def _chunk_seed(seed: int, tid: int, chunk: int) -> int:

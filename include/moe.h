@@ -211,6 +211,46 @@ moe_status_t moe_experts_down_fp8(const moe_desc_t* desc, const void* H, const i
 moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t* slot_pos,
                          const float* topk_w, void* out, void* stream);
 
+/* ---- Expert-choice routing ("Mixture of Experts (MoE) memo", routing section: the
+ * expert-choice row of the routing-design table, every expert picks the tokens that suit
+ * it and loads come out equal; "Mixture-of-experts in practice", top-k section: each
+ * expert takes its top-C tokens by its capacity, no token is dropped for capacity, and a
+ * token's routing depends on the whole batch, so it fits encoders, not causal decoding).
+ *   p[t, :]  = softmax(x[t] W_router^T) (no selection bias)
+ *   C        = min(T, max(floor(capacity_factor * top_k * T / E), top_k)), top_k read as
+ *              the average number of experts per token; capacity_factor must be > 0
+ *   expert e takes the C tokens with the largest p[t, e] (float32; equal values go to the
+ *   lower token index) as rows [e C, (e + 1) C) of the grouped GEMMs, in ascending token
+ *   order;
+ *   out[t]   = sum over the experts e that took t, ascending, of p[t, e] * FFN_e(x[t])
+ *              (+ the shared expert, weight 1); a token no expert took gives 0 (+ shared).
+ *   f_e = C / (E C) (1/E), P_e = mean_t p[t, e].
+ * Tensors and errors as for token choice; in addition a capacity_factor <= 0 is
+ * MOE_E_SHAPE and T > 32768 is MOE_E_UNSUPPORTED.  The workspace comes from
+ * moe_workspace_bytes_expert_choice (0 for an invalid description). */
+size_t moe_workspace_bytes_expert_choice(const moe_desc_t* desc);
+/* C as above, or -1 for an invalid description. */
+int64_t moe_capacity_expert_choice(const moe_desc_t* desc);
+/* Router probabilities probs [T, E] float32, the selection as offsets [E + 1] (e C),
+ * perm_src [E C] (token of each row) and slot [T, E] (row of (t, e), or -1), f and P
+ * (each optional, [E]).  Needs the workspace. */
+moe_status_t moe_route_expert_choice(const moe_desc_t* desc, const void* x,
+                                     const void* W_router, float* probs, int32_t* offsets,
+                                     int32_t* perm_src, int32_t* slot, float* f, float* p,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+/* out[t] = sum_{e ascending, slot[t, e] >= 0} probs[t, e] * Yp[slot[t, e]]
+ *          (+ Yp[E C + t] with a shared expert), float32 sums written in out_dtype. */
+moe_status_t moe_combine_expert_choice(const moe_desc_t* desc, const float* Yp,
+                                       const int32_t* slot, const float* probs, void* out,
+                                       void* stream);
+/* The whole layer with expert-choice routing (router, selection, grouped SwiGLU GEMMs
+ * over the E C rows and the shared expert's T rows, combine). */
+moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
+                                       const void* W_router, const void* W_gate,
+                                       const void* W_up, const void* W_down, void* out, float* f,
+                                       float* p, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,8 @@ kernels.  The functions mirror the C entry points:
 
     forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor, ...)
     route(...), dispatch(...), experts(...), combine(...)
+    forward_fp8(...) and the *_fp8 stages (8-bit expert weights)
+    forward_expert_choice(...), route_expert_choice(...), combine_expert_choice(...)
 
 There is no fallback: without the built library (python -m
 sparse_mixture_experts_24_amd.build) every call raises.
@@ -27,7 +29,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_UNSUPPORTED"
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_capacity",
            "moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_experts_gate_up",
            "moe_experts_down", "moe_combine", "moe_forward_fp8", "moe_experts_fp8",
-           "moe_experts_gate_up_fp8", "moe_experts_down_fp8")
+           "moe_experts_gate_up_fp8", "moe_experts_down_fp8",
+           "moe_workspace_bytes_expert_choice", "moe_capacity_expert_choice",
+           "moe_route_expert_choice", "moe_combine_expert_choice", "moe_forward_expert_choice")
 
 
 class MoeDesc(ctypes.Structure):
@@ -89,6 +93,16 @@ def lib():
         L.moe_experts_gate_up_fp8.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_experts_down_fp8.restype = I
         L.moe_experts_down_fp8.argtypes = [D, P, P, P, P, P, P, S, P]
+        L.moe_workspace_bytes_expert_choice.restype = S
+        L.moe_workspace_bytes_expert_choice.argtypes = [D]
+        L.moe_capacity_expert_choice.restype = ctypes.c_int64
+        L.moe_capacity_expert_choice.argtypes = [D]
+        L.moe_route_expert_choice.restype = I
+        L.moe_route_expert_choice.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_combine_expert_choice.restype = I
+        L.moe_combine_expert_choice.argtypes = [D, P, P, P, P, P]
+        L.moe_forward_expert_choice.restype = I
+        L.moe_forward_expert_choice.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         _lib = L
     return _lib
 
@@ -406,3 +420,88 @@ class MoELayer:
         return forward(x, self.W_router, self.router_bias, self.W_gate, self.W_up, self.W_down,
                        self.k, self.capacity_factor, out=out, f=f, p=p, out_dtype=self.out_dtype,
                        workspace=self._ws)
+
+
+# ----------------------------------------------------------------------------- expert choice
+def capacity_expert_choice(desc: MoeDesc) -> int:
+    """Tokens per expert under expert-choice routing (-1: invalid description)."""
+    return int(lib().moe_capacity_expert_choice(ctypes.byref(desc)))
+
+
+def alloc_workspace_expert_choice(desc: MoeDesc, device) -> torch.Tensor:
+    n = int(lib().moe_workspace_bytes_expert_choice(ctypes.byref(desc)))
+    if n == 0:
+        _check("moe_workspace_bytes_expert_choice", validate(desc) or 2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ws_ec(desc, device, workspace):
+    return alloc_workspace_expert_choice(desc, device) if workspace is None else workspace
+
+
+def forward_expert_choice(x, W_router, W_gate, W_up, W_down, k, capacity_factor, out=None,
+                          f=None, p=None, out_dtype=None, workspace=None):
+    """The layer with expert-choice routing: each expert takes its C tokens with the
+    largest router probability.  Returns (y, f, p)."""
+    dev = x.device
+    desc = desc_for(x, W_router, W_gate, k, capacity_factor, out_dtype)
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = W_gate.shape
+    for t, n, shp in ((x, "x", (T, d)), (W_router, "W_router", (E, d)),
+                      (W_gate, "W_gate", (G, F, d)), (W_up, "W_up", (G, F, d)),
+                      (W_down, "W_down", (G, d, F))):
+        _require(t, n, dev, x.dtype, shp)
+    odt = out_dtype or x.dtype
+    out = torch.empty(T, d, dtype=odt, device=dev) if out is None else out
+    f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+    p = torch.empty(E, dtype=torch.float32, device=dev) if p is None else p
+    _require(out, "out", dev, odt, (T, d))
+    ws = _ws_ec(desc, dev, workspace)
+    st = lib().moe_forward_expert_choice(ctypes.byref(desc), _ptr(x), _ptr(W_router),
+                                         _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(out),
+                                         _ptr(f), _ptr(p), _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_forward_expert_choice", st)
+    return out, f, p
+
+
+def route_expert_choice(x, W_router, k, capacity_factor, workspace=None):
+    """Router probabilities and the expert-choice selection.  Returns (probs [T, E],
+    offsets [E+1], perm_src [E C], slot [T, E], f [E], p [E])."""
+    dev = x.device
+    T, d = x.shape
+    E = W_router.shape[0]
+    desc = make_desc(T, d, E, 64, k, 0, capacity_factor, x.dtype)
+    _require(x, "x", dev)
+    _require(W_router, "W_router", dev, x.dtype, (E, d))
+    C = capacity_expert_choice(desc)
+    if C < 0:
+        _check("moe_capacity_expert_choice", validate(desc) or 2)
+    probs = torch.empty(T, E, dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(E * C, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(T, E, dtype=torch.int32, device=dev)
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    p = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws_ec(desc, dev, workspace)
+    st = lib().moe_route_expert_choice(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(probs),
+                                       _ptr(offsets), _ptr(perm), _ptr(slot), _ptr(f), _ptr(p),
+                                       _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_route_expert_choice", st)
+    return probs, offsets, perm[:E * C], slot, f, p
+
+
+def combine_expert_choice(Yp, slot, probs, d, k, capacity_factor, n_shared=0,
+                          out_dtype=torch.float32):
+    """out[t] = sum_e probs[t, e] Yp[slot[t, e]] over the experts that took t (+ shared)."""
+    dev = Yp.device
+    T, E = slot.shape
+    desc = make_desc(T, d, E, 64, k, n_shared, capacity_factor, torch.bfloat16, out_dtype)
+    out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    _require(Yp, "Yp", dev, torch.float32)
+    _require(slot, "slot", dev, torch.int32, (T, E))
+    _require(probs, "probs", dev, torch.float32, (T, E))
+    st = lib().moe_combine_expert_choice(ctypes.byref(desc), _ptr(Yp), _ptr(slot), _ptr(probs),
+                                         _ptr(out), _stream(dev))
+    _check("moe_combine_expert_choice", st)
+    return out

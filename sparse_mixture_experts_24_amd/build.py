@@ -17,7 +17,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip",
+           "expert_choice.hip"]
 ARCH = "gfx950"
 
 

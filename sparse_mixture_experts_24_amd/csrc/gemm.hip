@@ -1036,12 +1036,12 @@ static hipError_t run_f32(const GemmArgs& a, int64_t max_m_tiles, hipStream_t s)
   return hipGetLastError();
 }
 
-static GemmArgs base_args(const moe_desc_t& d, const int32_t* offsets) {
+static GemmArgs base_args(const moe_desc_t& d, const GemmRows& rows, const int32_t* offsets) {
   GemmArgs a{};
   a.offsets = offsets;
-  a.shared_row0 = d.T * d.top_k;
+  a.shared_row0 = rows.routed;
   a.T = (int)d.T;
-  a.topk = (int)d.top_k;
+  a.topk = rows.token_div;
   a.E = (int)d.n_experts;
   a.G = (int)(d.n_experts + d.n_shared);
   return a;
@@ -1050,8 +1050,8 @@ static GemmArgs base_args(const moe_desc_t& d, const int32_t* offsets) {
 // Dynamic tile order pays off where tile costs differ (large groups with 64-, 128- or
 // 256-row remainder tiles); for decode-sized batches (all groups small, every tile alike)
 // the counter round trip per tile is pure cost.
-static bool dynamic_tiles(const moe_desc_t& d) {
-  return d.T * d.top_k >= (int64_t)SMALL_GROUP_ROWS * d.n_experts;
+static bool dynamic_tiles(const moe_desc_t& d, const GemmRows& rows) {
+  return rows.routed >= (int64_t)SMALL_GROUP_ROWS * d.n_experts;
 }
 
 // Share of the CU slots of the last round left idle by n equal tiles on cus CUs.
@@ -1061,16 +1061,16 @@ static double idle_fraction(int64_t n, int64_t cus) {
   return (double)(slots - n) / (double)slots;
 }
 
-// Upper bound of sum_g ceil(M_g / bm): ceil(T*k / bm) + E (+ ceil(T / bm) shared).
-static int64_t max_m_tiles(const moe_desc_t& d, int bm) {
-  return ceil_div(d.T * d.top_k, bm) + d.n_experts + (d.n_shared ? ceil_div(d.T, bm) : 0);
+// Upper bound of sum_g ceil(M_g / bm): ceil(routed / bm) + E (+ ceil(T / bm) shared).
+static int64_t max_m_tiles(const moe_desc_t& d, const GemmRows& rows, int bm) {
+  return ceil_div(rows.routed, bm) + d.n_experts + (d.n_shared ? ceil_div(d.T, bm) : 0);
 }
 
-hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
-                          const int32_t* offsets, const ExpertWeights& ew, void* H, int32_t* ctr,
-                          hipStream_t s) {
+hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void* x,
+                          const int32_t* perm_src, const int32_t* offsets,
+                          const ExpertWeights& ew, void* H, int32_t* ctr, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, rows, offsets);
   a.A = x;
   a.perm_src = perm_src;
   a.B0 = ew.gate;
@@ -1082,19 +1082,19 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
   a.ksplit = 1;
-  a.ctr = dynamic_tiles(d) ? ctr : nullptr;
+  a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
   {
     // Every group fits a skinny tile (at most T rows each): take 64-column tiles when that
     // leaves less of the last round idle, e.g. 8 experts x 14336 columns give 896 tiles of
     // 128 (3.5 rounds of a 256-CU chip) but 1792 of 64 (7 rounds).
-    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, d.T * d.top_k + d.n_shared);
+    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, rows.routed + d.n_shared);
     const int64_t cus = device_cu_count();
     a.narrow_small = d.T <= SKINNY_ROWS &&
                      idle_fraction(groups * ceil_div(d.d_ff, 64), cus) + 0.02 <
                          idle_fraction(groups * ceil_div(d.d_ff, 128), cus);
   }
-  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_ff, 64);
-  if (!bf) return run_f32<true>(a, max_m_tiles(d, 64), s);
+  const int64_t mt = max_m_tiles(d, rows, BM_SMALL) * ceil_div(d.d_ff, 64);
+  if (!bf) return run_f32<true>(a, max_m_tiles(d, rows, 64), s);
   return ew.fp8 ? run_bf16<true, true>(a, mt, s) : run_bf16<true, false>(a, mt, s);
 }
 
@@ -1102,9 +1102,9 @@ hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* per
 // of 256 x 256 output tiles leaves the last round of a 256-CU chip at most 3/4 full and
 // doubling the work units saves at least a quarter of a round.  Host-only arithmetic
 // (no device query), so the workspace size depends on the description alone.
-bool down_split_k(const moe_desc_t& d) {
+bool down_split_k(const moe_desc_t& d, const GemmRows& rows) {
   if (d.dtype != MOE_DTYPE_BF16 || d.d_ff / BK < 2) return false;
-  const int64_t TK = d.T * d.top_k;
+  const int64_t TK = rows.routed;
   if (TK == 0) return false;
   const int64_t m_tiles = ceil_div(TK, BM_BIG) + std::min<int64_t>(d.n_experts, TK) +
                           (d.n_shared ? ceil_div(d.T, BM_BIG) : 0);
@@ -1114,11 +1114,11 @@ bool down_split_k(const moe_desc_t& d) {
   return r2 <= r1 - 0.25;
 }
 
-hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const ExpertWeights& ew, float* Yp, float* Yp2, int32_t* ctr,
-                       hipStream_t s) {
+hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
+                       const int32_t* offsets, const ExpertWeights& ew, float* Yp, float* Yp2,
+                       int32_t* ctr, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, rows, offsets);
   a.A = H;
   a.B0 = ew.down;
   a.sc0 = ew.s_down;
@@ -1129,14 +1129,14 @@ hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offset
   {
     // narrow down tiles for small groups only when even the most groups that can exist
     // would give fewer than two 256-column tiles per CU
-    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, d.T * d.top_k + d.n_shared);
+    const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, rows.routed + d.n_shared);
     a.narrow_small = groups * ceil_div(d.d_model, 256) < 2 * (int64_t)device_cu_count();
   }
   a.ksplit = (bf && Yp2) ? 2 : 1;
   a.out2 = Yp2;
-  a.ctr = dynamic_tiles(d) ? ctr : nullptr;
-  const int64_t mt = max_m_tiles(d, BM_SMALL) * ceil_div(d.d_model, 128);
-  if (!bf) return run_f32<false>(a, max_m_tiles(d, 64), s);
+  a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
+  const int64_t mt = max_m_tiles(d, rows, BM_SMALL) * ceil_div(d.d_model, 128);
+  if (!bf) return run_f32<false>(a, max_m_tiles(d, rows, 64), s);
   return ew.fp8 ? run_bf16<false, true>(a, mt, s) : run_bf16<false, false>(a, mt, s);
 }
 

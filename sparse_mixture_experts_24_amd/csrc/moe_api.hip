@@ -60,7 +60,8 @@ Workspace carve_workspace(const moe_desc_t& d, void* base) {
   w.bytes = off;   // the minimum; monotone in T
   // Optional tail: the second partial of a split down GEMM, used when the workspace has
   // room for it (moe_workspace_bytes asks for it).
-  w.Yp2 = down_split_k(d) ? (float*)take((size_t)rows * d.d_model * 4) : nullptr;
+  w.Yp2 = down_split_k(d, token_choice_rows(d)) ? (float*)take((size_t)rows * d.d_model * 4)
+                                                : nullptr;
   w.bytes_full = off;
   return w;
 }
@@ -122,8 +123,8 @@ static moe_status_t experts_impl(const moe_desc_t* desc, const void* x, const in
   hipStream_t s = (hipStream_t)stream;
   void* h = H ? H : w.H;
   MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
-  MOE_HIP(launch_gate_up(d, x, perm_src, offsets, ew, h, w.ctr, s));
-  MOE_HIP(launch_down(d, h, offsets, ew, Yp, nullptr, w.ctr + 8, s));
+  MOE_HIP(launch_gate_up(d, token_choice_rows(d), x, perm_src, offsets, ew, h, w.ctr, s));
+  MOE_HIP(launch_down(d, token_choice_rows(d), h, offsets, ew, Yp, nullptr, w.ctr + 8, s));
   return MOE_OK;
 }
 
@@ -151,7 +152,7 @@ static moe_status_t gate_up_impl(const moe_desc_t* desc, const void* x, const in
   if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (ctr) MOE_HIP(launch_zero_i32(ctr, 8, s));
-  MOE_HIP(launch_gate_up(*desc, x, perm_src, offsets, ew, H, ctr, s));
+  MOE_HIP(launch_gate_up(*desc, token_choice_rows(*desc), x, perm_src, offsets, ew, H, ctr, s));
   return MOE_OK;
 }
 
@@ -167,7 +168,8 @@ static moe_status_t down_impl(const moe_desc_t* desc, const void* H, const int32
   if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
-  MOE_HIP(launch_down(*desc, H, offsets, ew, Yp, nullptr, ctr ? ctr + 8 : nullptr, s));
+  MOE_HIP(launch_down(*desc, token_choice_rows(*desc), H, offsets, ew, Yp, nullptr,
+                      ctr ? ctr + 8 : nullptr, s));
   return MOE_OK;
 }
 
@@ -192,15 +194,78 @@ static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const vo
   const int E = (int)d.n_experts;
   const int64_t C = capacity_of(d);
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
-  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, w.p_part,
-                       w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, nullptr,
+                       w.p_part, w.cnt_part, s));
   MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
                              f, p, w.ctr, kTileCounters, s));
   MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
                          w.perm_src, w.slot_pos, s));
-  MOE_HIP(launch_gate_up(d, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
+  const GemmRows rows = token_choice_rows(d);
+  MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
   MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
+  return MOE_OK;
+}
+
+// ---- expert choice
+int64_t expert_choice_capacity(const moe_desc_t& d) {
+  const int64_t C = capacity_of(d);
+  if (C < 0) return -1;
+  return C < d.T ? C : d.T;
+}
+
+static GemmRows expert_choice_rows(const moe_desc_t& d) {
+  return {d.n_experts * expert_choice_capacity(d), 1};
+}
+
+// validate() plus what expert choice needs: a capacity factor > 0, T within the select
+// kernel's reach, and the E C + S T rows within 32-bit element offsets.
+static moe_status_t validate_ec(const moe_desc_t* d) {
+  moe_status_t st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!(d->capacity_factor > 0.0f)) return MOE_E_SHAPE;
+  if (d->T > kMaxExpertChoiceTokens) return MOE_E_UNSUPPORTED;
+  const int64_t rows = expert_choice_rows(*d).routed + d->n_shared * d->T;
+  if (rows > (int64_t)INT32_MAX || rows * d->d_ff > (int64_t)INT32_MAX ||
+      rows * d->d_model > (int64_t)INT32_MAX)
+    return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+WorkspaceEC carve_workspace_ec(const moe_desc_t& d, void* base) {
+  const RoutePlan rp = route_plan(d);
+  const GemmRows gr = expert_choice_rows(d);
+  const int64_t E = d.n_experts, TE = d.T * E;
+  const int64_t rows = gr.routed + d.n_shared * d.T;
+  const size_t esz = d.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  char* p = (char*)base;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? (void*)(p + off) : nullptr;
+    off += align256(bytes > 0 ? bytes : 1);
+    return r;
+  };
+  WorkspaceEC w{};
+  w.p_part = (float*)take(rp.n_blocks * E * 4);
+  w.cnt_part = (int32_t*)take(rp.n_blocks * E * 4);
+  w.counts = (int32_t*)take(E * 4);
+  w.ctr = (int32_t*)take(kTileCounters * 4);
+  w.offsets = (int32_t*)take((E + 1) * 4);
+  w.probs = (float*)take(TE * 4);
+  w.slot = (int32_t*)take(TE * 4);
+  w.perm_src = (int32_t*)take(gr.routed * 4);
+  w.H = take((size_t)rows * d.d_ff * esz);
+  w.Yp = (float*)take((size_t)rows * d.d_model * 4);
+  w.bytes = off;
+  w.Yp2 = down_split_k(d, gr) ? (float*)take((size_t)rows * d.d_model * 4) : nullptr;
+  w.bytes_full = off;
+  return w;
+}
+
+static moe_status_t check_ws_ec(const moe_desc_t& d, void* ws, size_t bytes, WorkspaceEC& w) {
+  w = carve_workspace_ec(d, ws);
+  if (!ws || bytes < w.bytes || ((uintptr_t)ws & 255u)) return MOE_E_WORKSPACE;
+  if (bytes < w.bytes_full) w.Yp2 = nullptr;
   return MOE_OK;
 }
 
@@ -248,8 +313,8 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const RoutePlan rp = route_plan(d);
-  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, gap, w.p_part, w.cnt_part,
-                       s));
+  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, gap, nullptr, w.p_part,
+                       w.cnt_part, s));
   if (f || p)
     MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
                                (int)d.top_k, w.counts, f, p, nullptr, 0, s));
@@ -354,6 +419,104 @@ moe_status_t moe_experts_down_fp8(const moe_desc_t* desc, const void* H, const i
                                   void* workspace, size_t workspace_bytes, void* stream) {
   const ExpertWeights ew{nullptr, nullptr, Wq_down, nullptr, nullptr, s_down, true};
   return down_impl(desc, H, offsets, ew, Yp, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- expert-choice routing
+extern "C" {
+
+size_t moe_workspace_bytes_expert_choice(const moe_desc_t* desc) {
+  if (validate_ec(desc) != MOE_OK) return 0;
+  return carve_workspace_ec(*desc, nullptr).bytes_full;
+}
+
+int64_t moe_capacity_expert_choice(const moe_desc_t* desc) {
+  if (validate_ec(desc) != MOE_OK) return -1;
+  return expert_choice_capacity(*desc);
+}
+
+moe_status_t moe_route_expert_choice(const moe_desc_t* desc, const void* x,
+                                     const void* W_router, float* probs, int32_t* offsets,
+                                     int32_t* perm_src, int32_t* slot, float* f, float* p,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate_ec(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!W_router || !offsets || (d.T > 0 && (!x || !probs || !perm_src || !slot)))
+    return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_router)) return MOE_E_UNSUPPORTED;
+  WorkspaceEC w;
+  if ((st = check_ws_ec(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  const int E = (int)d.n_experts;
+  if (d.T == 0) {   // no tokens: empty groups, f and P zero
+    MOE_HIP(launch_zero_i32(offsets, E + 1, s));
+    if (f || p)
+      MOE_HIP(launch_expert_scan(w.cnt_part, 0, E, nullptr, 0, (int)d.top_k, w.counts, f, p,
+                                 nullptr, 0, s));
+    return MOE_OK;
+  }
+  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, probs, w.p_part,
+                       w.cnt_part, s));
+  if (p)
+    MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k,
+                               w.counts, nullptr, p, nullptr, 0, s));
+  MOE_HIP(launch_ec_select(probs, (int)d.T, E, (int)expert_choice_capacity(d), perm_src, offsets,
+                           slot, f, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_combine_expert_choice(const moe_desc_t* desc, const float* Yp,
+                                       const int32_t* slot, const float* probs, void* out,
+                                       void* stream) {
+  moe_status_t st = validate_ec(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (d.T > 0 && (!Yp || !slot || !probs || !out)) return MOE_E_NULL;
+  if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
+  MOE_HIP(launch_ec_combine(d, expert_choice_rows(d).routed, Yp, nullptr, slot, probs, out,
+                            (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
+                                       const void* W_router, const void* W_gate,
+                                       const void* W_up, const void* W_down, void* out, float* f,
+                                       float* p, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  moe_status_t st = validate_ec(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!W_router || !W_gate || !W_up || !W_down || (d.T > 0 && (!x || !out))) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_router) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down) || !aligned16(out))
+    return MOE_E_UNSUPPORTED;
+  WorkspaceEC w;
+  if ((st = check_ws_ec(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  const int E = (int)d.n_experts;
+  const GemmRows rows = expert_choice_rows(d);
+  const ExpertWeights ew = plain_weights(W_gate, W_up, W_down);
+  if (d.T == 0) {   // no tokens: f and P are zero
+    if (f || p)
+      MOE_HIP(launch_expert_scan(w.cnt_part, 0, E, nullptr, 0, (int)d.top_k, w.counts, f, p,
+                                 nullptr, 0, s));
+    return MOE_OK;
+  }
+  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, w.probs, w.p_part,
+                       w.cnt_part, s));
+  // P from the route blocks' partial sums; also clears the GEMMs' work counters
+  MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
+                             nullptr, p, w.ctr, kTileCounters, s));
+  MOE_HIP(launch_ec_select(w.probs, (int)d.T, E, (int)expert_choice_capacity(d), w.perm_src,
+                           w.offsets, w.slot, f, s));
+  MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
+  MOE_HIP(launch_ec_combine(d, rows.routed, w.Yp, w.Yp2, w.slot, w.probs, out, s));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -54,13 +54,34 @@ struct Workspace {
 };
 Workspace carve_workspace(const moe_desc_t& d, void* base);
 
+// Expert-choice layers: probabilities and slot matrix [T, E], E*C routed rows.
+struct WorkspaceEC {
+  float* p_part;       // [route blocks][E]
+  int32_t* cnt_part;   // [route blocks][E]
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]
+  float* probs;        // [T, E]
+  int32_t* slot;       // [T, E]
+  int32_t* perm_src;   // [E*C]
+  void* H;             // [E*C + S*T, F] dtype
+  float* Yp;           // [E*C + S*T, d]
+  int32_t* ctr;        // kTileCounters
+  float* Yp2;          // or NULL
+  size_t bytes, bytes_full;
+};
+// C of an expert-choice layer: min(T, max(floor(cf k T / E), k)); -1 when cf <= 0.
+int64_t expert_choice_capacity(const moe_desc_t& d);
+WorkspaceEC carve_workspace_ec(const moe_desc_t& d, void* base);
+
 constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe_dispatch
 
 // ---------------------------------------------------------------- launchers
 // gap (optional, [T]): s_(k) - s_(k+1) of each token's selection scores (+inf if k == E).
+// probs (optional, [T, E]): the router probabilities.  With topk_idx NULL no top-k is
+// taken (and the block histograms stay zero).
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
-                        float* p_part, int32_t* cnt_part, hipStream_t s);
+                        float* probs, float* p_part, int32_t* cnt_part, hipStream_t s);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
 // zero (optional): nzero <= 256 int32 that block 0 also sets to zero.
@@ -81,20 +102,40 @@ struct ExpertWeights {
   const float* s_down;   // [E + S, d]
   bool fp8;
 };
-hipError_t launch_gate_up(const moe_desc_t& d, const void* x, const int32_t* perm_src,
-                          const int32_t* offsets, const ExpertWeights& ew, void* H, int32_t* ctr,
-                          hipStream_t s);
+// Rows of the grouped GEMMs: `routed` expert-contiguous rows (offsets[E] of them at most),
+// row r taking token perm_src[r] / token_div, then the shared expert's T rows.
+struct GemmRows {
+  int64_t routed;   // T*k (token choice) or E*C (expert choice)
+  int token_div;    // k (perm_src holds t*k + j) or 1 (perm_src holds t)
+};
+inline GemmRows token_choice_rows(const moe_desc_t& d) { return {d.T * d.top_k, (int)d.top_k}; }
+hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void* x,
+                          const int32_t* perm_src, const int32_t* offsets,
+                          const ExpertWeights& ew, void* H, int32_t* ctr, hipStream_t s);
 // Yp2 non-NULL (bf16 layers): K split in two, partial sums in Yp and Yp2.
 // ctr: NULL (static tile order) or 8 int32 work counters, zero at launch.
-hipError_t launch_down(const moe_desc_t& d, const void* H, const int32_t* offsets,
-                       const ExpertWeights& ew, float* Yp, float* Yp2, int32_t* ctr,
-                       hipStream_t s);
+hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
+                       const int32_t* offsets, const ExpertWeights& ew, float* Yp, float* Yp2,
+                       int32_t* ctr, hipStream_t s);
 // Sets n int32 to zero (a kernel, so that it may sit in a captured graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 constexpr int kTileCounters = 16;   // 8 per grouped GEMM
-bool down_split_k(const moe_desc_t& d);
+bool down_split_k(const moe_desc_t& d, const GemmRows& rows);
 // Yp2 non-NULL: the per-slot outputs are Yp + Yp2.
 hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
                           const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s);
+
+// Expert choice: expert e takes the C tokens with the largest probs[:, e] (ties to the
+// lower token), rows [e C, (e+1) C) in ascending token order; slot [T, E] gets each
+// (token, expert)'s row or -1; f (optional) the share of the E*C assignments.
+// Needs T <= kMaxExpertChoiceTokens.
+constexpr int kMaxExpertChoiceTokens = 32768;
+hipError_t launch_ec_select(const float* probs, int T, int E, int C, int32_t* perm_src,
+                            int32_t* offsets, int32_t* slot, float* f, hipStream_t s);
+// out[t] = sum over e ascending with slot[t, e] >= 0 of probs[t, e] * Yp[slot[t, e]]
+// (+ Yp[shared_row0 + t] with a shared expert); Yp2 as in launch_combine.
+hipError_t launch_ec_combine(const moe_desc_t& d, int64_t shared_row0, const float* Yp,
+                             const float* Yp2, const int32_t* slot, const float* probs,
+                             void* out, hipStream_t s);
 
 }  // namespace moe

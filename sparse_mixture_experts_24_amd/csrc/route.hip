@@ -99,12 +99,13 @@ __device__ inline void wave_argmax(float& v, int& e) {
 
 // Softmax + top-k + renorm for the tokens of one block, logits in LDS rows of E_PAD.
 // Waves take tokens tt = wave, wave + 4, ...  Accumulates p into psum (per lane, expert
-// lane + 64 i) and the chosen experts into the LDS histogram cnt.
+// lane + 64 i) and the chosen experts into the LDS histogram cnt.  probs (optional)
+// receives every p; k = 0 takes no top-k.
 template <int E_PAD>
 __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E, int k,
                                   const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
                                   float* __restrict__ topk_w, float* __restrict__ gap,
-                                  float* psum, int* cnt) {
+                                  float* __restrict__ probs, float* psum, int* cnt) {
   constexpr int NV = (E_PAD + 63) / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bv[NV];
@@ -142,6 +143,7 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
       v[i] = v[i] * inv;                       // p
       psum[i] += v[i];
       s[i] = (e < E) ? v[i] + bv[i] : -INFINITY;   // selection score, fp32
+      if (probs != nullptr && e < E) probs[(size_t)t * E + e] = v[i];
     }
     unsigned taken = 0;
     int my_idx = 0;
@@ -208,7 +210,8 @@ template <int EPW, int TPW, int KS, int R>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ gap, float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ probs, float* __restrict__ p_part,
+    int32_t* __restrict__ cnt_part) {
   constexpr int EW = 4 / KS;
   constexpr int E_PAD = 16 * EPW * EW;
   constexpr int BT = 16 * TPW;
@@ -311,7 +314,8 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, psum, cnt);
+  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, psum,
+                    cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -321,7 +325,8 @@ template <int E_PAD>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ gap, float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ probs, float* __restrict__ p_part,
+    int32_t* __restrict__ cnt_part) {
   constexpr int BT = 16;
   constexpr int NV = (E_PAD + 63) / 64;
   __shared__ float lg[BT][E_PAD];
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, psum, cnt);
+  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -389,10 +394,11 @@ RoutePlan route_plan(const moe_desc_t& d) {
 
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
-                        float* p_part, int32_t* cnt_part, hipStream_t s) {
+                        float* probs, float* p_part, int32_t* cnt_part, hipStream_t s) {
   const RoutePlan rp = route_plan(d);
   if (rp.n_blocks == 0) return hipSuccess;
-  const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts, k = (int)d.top_k;
+  const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts;
+  const int k = topk_idx != nullptr ? (int)d.top_k : 0;
   const dim3 grid((unsigned)rp.n_blocks), block(256);
   if (d.dtype == MOE_DTYPE_F32) {
     const float* xx = (const float*)x;
@@ -400,7 +406,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
 #define MOE_ROUTE_F32(EP)                                                                     \
   if (rp.E_pad == EP) {                                                                       \
     hipLaunchKernelGGL(route_f32_kernel<EP>, grid, block, 0, s, xx, ww, bias, T, dm, E, k,    \
-                       topk_idx, topk_w, gap, p_part, cnt_part);                              \
+                       topk_idx, topk_w, gap, probs, p_part, cnt_part);                       \
     return hipGetLastError();                                                                 \
   }
     MOE_ROUTE_F32(64)
@@ -418,7 +424,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
     constexpr int R_ = (EPW_ + TPW_) <= 3 ? 8 : 200 / (8 * (EPW_ + TPW_));                      \
     hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, R_>), grid, block, 0, s, xx, ww,   \
-                       bias, T, dm, E, k, topk_idx, topk_w, gap, p_part, cnt_part);           \
+                       bias, T, dm, E, k, topk_idx, topk_w, gap, probs, p_part, cnt_part);    \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTE_BF16(1, 1, 4)

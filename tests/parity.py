@@ -210,3 +210,63 @@ def _check_h_only(H_gpu, parts, x, Wg, Wu, what=""):
     H_gpu = np.asarray(H_gpu, np.float64)
     out = (H_gpu < np.minimum(lo, hi)) | (H_gpu > np.maximum(lo, hi))
     assert not out.any(), f"{what}: {out.sum()} h values are no rounding of [h-dh, h+dh]"
+
+
+def check_expert_choice(perm_gpu, offsets_gpu, slot_gpu, probs_ref, sel_ref, margin, C):
+    """Expert-choice selection: each expert's tokens bit-exact wherever the oracle's margin
+    (C-th minus (C+1)-th largest probability) is >= 1e-6; a near-tied expert's tokens must
+    still be C distinct tokens, ascending, none below the C-th largest probability by more
+    than 1e-6.  offsets are e*C and slot is the inverse of perm.  Returns the GPU's
+    selection [E, C]."""
+    T, E = probs_ref.shape
+    perm_gpu = np.asarray(perm_gpu)[:E * C].reshape(E, C)
+    assert np.array_equal(np.asarray(offsets_gpu), np.arange(E + 1) * C)
+    for e in range(E):
+        if margin[e] >= NEAR_TIE:
+            assert np.array_equal(perm_gpu[e], sel_ref[e]), f"expert {e} took other tokens"
+        else:
+            col = probs_ref[:, e].astype(np.float64)
+            kth = np.sort(col)[::-1][C - 1]
+            assert len(set(perm_gpu[e].tolist())) == C
+            assert np.all(col[perm_gpu[e]] >= kth - NEAR_TIE)
+        assert np.all(np.diff(perm_gpu[e]) > 0), f"expert {e}: rows not in token order"
+    slot_ref = np.full((T, E), -1, np.int64)
+    for e in range(E):
+        slot_ref[perm_gpu[e], e] = e * C + np.arange(C)
+    assert np.array_equal(np.asarray(slot_gpu), slot_ref)
+    return perm_gpu
+
+
+def expert_choice_rows_reference(inp, rows, sel, probs, n_shared, h_bf16):
+    """Like expert_rows_reference, for expert choice: token rows[i] gets p[t, e] * o_e for
+    every expert e whose selection holds it (row e*C + its rank), plus the shared expert
+    (row E*C + t)."""
+    x = np32(inp["x"])
+    T, d = x.shape
+    E, C = sel.shape
+    rows = np.asarray(rows, np.int64)
+    items = []
+    for e in range(E):
+        pos = {int(t): e * C + r for r, t in enumerate(sel[e])}
+        hit = [i for i, t in enumerate(rows) if int(t) in pos]
+        if not hit:
+            continue
+        Wg, Wu, Wd = oracle.expert_weights(inp, e)
+        o, parts = oracle.expert_ffn(x[rows[hit]], Wg, Wu, Wd, h_bf16, return_h=True)
+        for q, i in enumerate(hit):
+            t = int(rows[i])
+            items.append((i, float(probs[t, e]), e, pos[t],
+                          {key: v[q:q + 1] for key, v in parts.items()}, o[q:q + 1],
+                          x[t:t + 1], (Wg, Wu, Wd)))
+    if n_shared:
+        Wg, Wu, Wd = oracle.expert_weights(inp, E)
+        o, parts = oracle.expert_ffn(x[rows], Wg, Wu, Wd, h_bf16, return_h=True)
+        for i in range(rows.size):
+            items.append((i, 1.0, E, E * C + int(rows[i]),
+                          {key: v[i:i + 1] for key, v in parts.items()}, o[i:i + 1],
+                          x[rows[i]:rows[i] + 1], (Wg, Wu, Wd)))
+    items.sort(key=lambda it: (it[0], it[2]))      # per row, experts ascending
+    y = np.zeros((rows.size, d))
+    for i, wt, e, pos, parts, o, xr, W in items:
+        y[i] += wt * o[0].astype(np.float64)
+    return y.astype(np.float32), items

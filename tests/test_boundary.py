@@ -148,3 +148,33 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe.so")
     with pytest.raises(ImportError):
         moe.lib()
+
+
+def test_expert_choice_validation_and_capacity(L):
+    """Expert choice needs a capacity factor > 0 and T within the select kernel's reach;
+    its C is the token-choice capacity capped at T."""
+    for T, E, k, cf in [(4096, 8, 2, 1.0), (10, 8, 2, 1.0), (10, 8, 2, 50.0), (1, 4, 1, 0.5),
+                        (16384, 64, 1, 1.25)]:
+        d = desc(T=T, n_experts=E, top_k=k, capacity_factor=cf)
+        assert L.moe_capacity_expert_choice(ctypes.byref(d)) == oracle.expert_choice_capacity(
+            T, k, E, cf)
+        assert L.moe_workspace_bytes_expert_choice(ctypes.byref(d)) > 0
+    for kw, status in [({"capacity_factor": 0.0}, 2), ({"capacity_factor": -1.0}, 2),
+                       ({"T": 32769, "capacity_factor": 1.0}, 3)]:
+        d = desc(**kw)
+        assert L.moe_capacity_expert_choice(ctypes.byref(d)) == -1
+        assert L.moe_workspace_bytes_expert_choice(ctypes.byref(d)) == 0
+        fake = ctypes.c_void_p(0x100000)
+        assert L.moe_forward_expert_choice(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
+                                           None, None, fake, 1 << 30, None) == status
+    d = desc(capacity_factor=1.0)
+    need = L.moe_workspace_bytes_expert_choice(ctypes.byref(d))
+    fake = ctypes.c_void_p(0x100000)
+    assert L.moe_forward_expert_choice(ctypes.byref(d), None, fake, fake, fake, fake, fake,
+                                       None, None, fake, need, None) == 1
+    assert L.moe_forward_expert_choice(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
+                                       None, None, fake, need // 4, None) == 4
+    assert L.moe_route_expert_choice(ctypes.byref(d), fake, fake, None, fake, fake, fake, None,
+                                     None, fake, need, None) == 1
+    assert L.moe_combine_expert_choice(ctypes.byref(d), fake, None, fake, fake, None) == 1
+    assert L.moe_combine_expert_choice(ctypes.byref(desc()), fake, fake, fake, fake, None) == 2

@@ -83,3 +83,15 @@ def test_fp8_workload_stores_codes_and_row_scales():
         bound = torch.maximum(W.abs() * 2.0 ** -4, inp["s_" + name][..., None] * 2.0 ** -10)
         assert ((deq - W).abs() <= bound * (1 + 1e-6)).all()
     assert torch.equal(inp["x"], ref["x"]) and torch.equal(inp["W_router"], ref["W_router"])
+
+
+def test_expert_choice_workload_shares_the_prefill_inputs():
+    """The expert-choice prefill workload draws the prefill layer's tensors (same seeds)
+    and only changes the routing: C = T k / E tokens per expert."""
+    a, b = gen.workload("mixtral_prefill"), gen.workload("mixtral_prefill_ec")
+    assert b.routing == "expert" and a.routing == "token"
+    assert (b.T, b.d, b.E, b.k, b.F, b.row_scales) == (a.T, a.d, a.E, a.k, a.F, a.row_scales)
+    assert oracle.expert_choice_capacity(b.T, b.k, b.E, b.capacity_factor) == 1024
+    sa = gen.make_inputs(a.replace(T=32, d=64, F=64), parts=("x", "W_router"))
+    sb = gen.make_inputs(b.replace(T=32, d=64, F=64), parts=("x", "W_router"))
+    assert torch.equal(sa["x"], sb["x"]) and torch.equal(sa["W_router"], sb["W_router"])
