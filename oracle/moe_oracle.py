@@ -30,6 +30,10 @@ notes of the repository):
   * capacity C = max(floor(cf * k * T / E), k); assignments are ranked per expert in
     row-major (token, slot) order and the first C are kept;
   * a dropped assignment contributes zero; the layer adds no residual;
+  * overflow handed to the next-best expert ([book ch.30] 30.5.2) is one redirect round:
+    each assignment dropped by the capacity goes to its token's next unused expert by
+    selection score, which takes such offers in row-major order while it has room; the
+    slot keeps its weight;
   * 8-bit expert weights (an extension past the pages' layer: [book ch.30] 30.4.6 counts
     FP8 among the measures that halve the memory traffic of each operation, and
     [MoE practice], section on quantisation and routing, keeps the router in high
@@ -287,13 +291,15 @@ def expert_weights(inputs: dict, e: int):
 
 
 def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
-            h_bf16: bool = True, idx_override=None) -> dict:
+            h_bf16: bool = True, idx_override=None, next_best: bool = False) -> dict:
     """The whole layer: route -> stats -> dispatch -> grouped experts -> combine.
 
     ``inputs`` holds x, W_router, router_bias (or None), W_gate, W_up, W_down as torch
     tensors or float32 arrays.  ``idx_override`` replaces the top-k choice (used where
     near-tied tokens have more than one correct routing); the weights are then
-    renormalised from the same unbiased probabilities.
+    renormalised from the same unbiased probabilities.  ``next_best`` hands assignments
+    that overflow an expert's capacity to their token's next-best experts
+    (``dispatch_next_best``) instead of dropping them.
     """
     x = _np(inputs["x"])
     Wr = _np(inputs["W_router"])
@@ -306,7 +312,11 @@ def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 
         r["w"] = renorm_weights(r["p"], r["idx"])
     f, P = aux_stats(r["p"], r["idx"], E)
     C = capacity(T, k, E, capacity_factor)
-    disp = dispatch(r["idx"], E, C)
+    if next_best:
+        r["cand"] = next_best_candidates(r["s"], k, r["idx"])
+        disp = dispatch_next_best(r["idx"], r["cand"], E, C)
+    else:
+        disp = dispatch(r["idx"], E, C)
     Y = np.zeros((int(disp["offsets"][-1]), d), F32)
     for e in range(E):
         lo, hi = int(disp["offsets"][e]), int(disp["offsets"][e + 1])
@@ -339,7 +349,9 @@ def forward_rows(inputs: dict, rows, k: int, capacity_factor: float = 0.0,
         disp = dispatch(routing["idx"], E, capacity(T, k, E, capacity_factor))
     rows = np.asarray(rows, np.int64)
     sp = disp["slot_pos"].reshape(T, k)[rows]
-    idx = routing["idx"][rows]
+    # the expert that processes each slot (differs from the top-k choice for redirected
+    # slots)
+    idx = disp["expert"].reshape(T, k)[rows] if "expert" in disp else routing["idx"][rows]
     w = routing["w"][rows]
     y = np.zeros((rows.size, d), F64)
     for e in np.unique(idx[sp >= 0]):
@@ -436,3 +448,81 @@ def forward_expert_choice(inputs: dict, k: int, capacity_factor: float, n_shared
     P = p.astype(F64).mean(axis=0).astype(F32)
     return {"y": y, "f": f, "p": P, "probs": p, "sel": sel, "margin": margin, "C": C,
             "dispatch": disp}
+
+
+# ----------------------------------------------------------------------------- next best
+def next_best_candidates(s: np.ndarray, k: int, idx: np.ndarray | None = None) -> np.ndarray:
+    """The experts each token would take after its k chosen ones: its best selection
+    scores outside its top-k (descending, ties to the lower expert index), at most k of
+    them, -1 where fewer than k experts remain.  With ``idx`` (a given top-k choice) the
+    candidates are the best-scored experts outside idx."""
+    T, E = s.shape
+    s2 = s.astype(F64).copy()
+    if idx is None:
+        idx = np.argsort(-s2, axis=1, kind="stable")[:, :k]
+    np.put_along_axis(s2, np.asarray(idx, np.int64), -np.inf, axis=1)
+    order = np.argsort(-s2, axis=1, kind="stable")     # the chosen experts sort last
+    cand = np.full((T, k), -1, np.int32)
+    m = min(k, E - k)
+    cand[:, :m] = order[:, :m]
+    return cand
+
+
+def dispatch_next_best(idx: np.ndarray, cand: np.ndarray, E: int, C: int) -> dict:
+    """Capacity overflow handed to the next-best expert instead of dropped.
+
+    [book ch.30] 30.5.2: tokens past an expert's capacity are dropped or redirected to
+    the next-best expert.  Reading: one redirect round.  Round 0 is ``dispatch``: each
+    expert keeps its first C assignments in row-major (token, slot) order.  Every
+    assignment dropped there is offered to its token's next-best expert: the m-th dropped
+    slot of token t (in slot order) goes to cand[t, m], the token's (k+1+m)-th best
+    expert.  Each expert takes these offers in row-major order while its total stays
+    within C; the rest are dropped.  An expert's rows are its round-0 assignments, then the
+    redirected ones, each in row-major order.  The slot keeps its mixing weight.
+
+    Returns the fields of ``dispatch`` (counts = the top-k histogram, kept = rows per
+    expert) plus expert [T*k]: the expert that processes each assignment (-1 dropped).
+    """
+    if C is None:
+        raise ValueError("redirecting overflow needs a capacity")
+    T, k = idx.shape
+    d0 = dispatch(idx, E, C)
+    flat = idx.reshape(-1).astype(np.int64)
+    sp0 = d0["slot_pos"].astype(np.int64)
+    kept0 = d0["kept"].astype(np.int64)
+    rank0 = np.where(sp0 >= 0, sp0 - d0["offsets"].astype(np.int64)[np.clip(flat, 0, E - 1)], -1)
+    dropped = (sp0 < 0).reshape(T, k)
+    m = np.cumsum(dropped, axis=1) - dropped                  # earlier dropped slots of t
+    cand = np.asarray(cand, np.int64)
+    mm = np.minimum(m, cand.shape[1] - 1)
+    prop = np.where(dropped & (m < cand.shape[1]), np.take_along_axis(cand, mm, axis=1), -1)
+    prop = prop.reshape(-1)
+    # stable rank of each offer among the offers to the same expert, row-major order
+    offered = np.nonzero(prop >= 0)[0]
+    tgt = prop[offered]
+    order = np.argsort(tgt, kind="stable")
+    pcount = np.bincount(tgt, minlength=E).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(pcount)[:-1]])
+    rank1 = np.empty(offered.size, np.int64)
+    rank1[order] = np.arange(offered.size) - start[tgt[order]]
+    room = C - kept0
+    acc = rank1 < room[tgt]
+    acc_count = np.bincount(tgt[acc], minlength=E).astype(np.int64)
+    kept = kept0 + acc_count
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    slot_pos = np.full(T * k, -1, np.int64)
+    expert = np.full(T * k, -1, np.int64)
+    keep0 = sp0 >= 0
+    slot_pos[keep0] = offsets[flat[keep0]] + rank0[keep0]
+    expert[keep0] = flat[keep0]
+    a_i, a_e = offered[acc], tgt[acc]
+    slot_pos[a_i] = offsets[a_e] + kept0[a_e] + rank1[acc]
+    expert[a_i] = a_e
+    perm_src = np.empty(int(offsets[-1]), np.int64)
+    perm_src[slot_pos[slot_pos >= 0]] = np.nonzero(slot_pos >= 0)[0]
+    return {
+        "counts": d0["counts"], "kept": kept.astype(np.int32),
+        "offsets": offsets.astype(np.int32), "perm_src": perm_src.astype(np.int32),
+        "slot_pos": slot_pos.astype(np.int32), "expert": expert.astype(np.int32),
+        "redirected": int(acc.sum()),
+    }

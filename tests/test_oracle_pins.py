@@ -628,3 +628,163 @@ def test_expert_choice_planted_mistakes_are_caught(monkeypatch):
         assert _pins_fail(lambda: test_expert_choice_forward_matches_per_token_loop(
             24, 16, 6, 2, 20, 0, 1.0, False))
     assert orig_probs is mo.router_probs
+
+
+# --------------------------------------------------------------------------- next best
+def brute_next_best(idx, s, E, C):
+    """Sequential formulation: per-expert load counters; first every assignment in
+    row-major order takes its top-k expert if it has room; then every assignment that
+    found none, in row-major order, takes its token's next unused expert by score (the
+    m-th such slot of the token its (k+1+m)-th best) if that one has room."""
+    T, k = idx.shape
+    load = [0] * E
+    final = [[-1] * k for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if load[e] < C:
+                load[e] += 1
+                final[t][j] = e
+    for t in range(T):
+        ranked = sorted(range(E), key=lambda e: (-float(s[t, e]), e))
+        rest = [e for e in ranked if e not in set(int(v) for v in idx[t])]
+        m = 0
+        for j in range(k):
+            if final[t][j] >= 0:
+                continue
+            if m < len(rest) and m < k:
+                e = rest[m]
+                if load[e] < C:
+                    load[e] += 1
+                    final[t][j] = e
+            m += 1
+    return np.array(final, np.int64)
+
+
+def test_next_best_hand_example():
+    """3 experts, C = 1: tokens 0-2 pick expert 0, token 3 expert 1.  Token 0 keeps
+    expert 0; token 1 moves to its next best, expert 2; token 2's next best, expert 1, is
+    full, so it is dropped."""
+    idx = np.array([[0], [0], [0], [1]])
+    s = np.array([[.5, .3, .2], [.6, .1, .3], [.7, .2, .1], [.1, .8, .1]], np.float32)
+    cand = oracle.next_best_candidates(s, 1, idx)
+    assert cand.ravel().tolist() == [1, 2, 1, 0]
+    d = oracle.dispatch_next_best(idx, cand, 3, 1)
+    assert d["expert"].tolist() == [0, 2, -1, 1]
+    assert d["offsets"].tolist() == [0, 1, 2, 3]
+    assert d["perm_src"].tolist() == [0, 3, 1]
+    assert d["slot_pos"].tolist() == [0, 2, -1, 1]
+
+
+@pytest.mark.parametrize("T,E,k,C,seed", [(40, 6, 2, 9, 0), (64, 8, 1, 5, 1), (30, 5, 3, 20, 2),
+                                          (25, 4, 2, 15, 3), (25, 4, 2, 3, 3), (50, 16, 4, 14, 4)])
+def test_next_best_matches_sequential_loop(T, E, k, C, seed):
+    rng = np.random.default_rng(seed)
+    s = (rng.integers(0, 9, (T, E)) / 16.0 + rng.random((T, E)) * 1e-3).astype(np.float32)
+    s[:, 0] += 0.5                                   # skew: expert 0 overflows
+    idx = np.argsort(-s.astype(np.float64), axis=1, kind="stable")[:, :k]
+    d = oracle.dispatch_next_best(idx, oracle.next_best_candidates(s, k, idx), E, C)
+    final = brute_next_best(idx, s, E, C)
+    np.testing.assert_array_equal(d["expert"].reshape(T, k), final)
+    kept = np.bincount(final[final >= 0], minlength=E)
+    assert (kept <= C).all()
+    np.testing.assert_array_equal(np.diff(d["offsets"]), kept)
+    for t in range(T):                               # never two rows of one expert per token
+        used = final[t][final[t] >= 0]
+        assert len(set(used.tolist())) == used.size
+    # rows: round-0 assignments, then the redirected ones, each in row-major order
+    for e in range(E):
+        rows = d["perm_src"][d["offsets"][e]:d["offsets"][e + 1]]
+        moved = np.array([idx.reshape(-1)[i] != e for i in rows])
+        assert not (moved[:-1] & ~moved[1:]).any()
+        assert np.all(np.diff(rows[~moved]) > 0) and np.all(np.diff(rows[moved]) > 0)
+    if E * C >= T * k:                               # room left somewhere: some moved
+        assert d["redirected"] > 0
+
+
+def test_next_best_reduces_to_dispatch():
+    """Without overflow, or with no candidate left, nothing moves."""
+    rng = np.random.default_rng(5)
+    T, E, k = 40, 6, 2
+    s = rng.random((T, E)).astype(np.float32)
+    idx = np.argsort(-s.astype(np.float64), axis=1, kind="stable")[:, :k]
+    for C, cand in [(T * k, oracle.next_best_candidates(s, k, idx)),
+                    (4, np.full((T, k), -1, np.int32))]:
+        a = oracle.dispatch_next_best(idx, cand, E, C)
+        b = oracle.dispatch(idx, E, C)
+        for key in ("offsets", "perm_src", "slot_pos"):
+            np.testing.assert_array_equal(a[key], b[key])
+
+
+def per_token_next_best(inp, k, cf, h_bf16):
+    """The layer with redirected overflow, one token at a time over brute_next_best."""
+    x = inp["x"].astype(np.float64)
+    T, d = x.shape
+    E = inp["W_router"].shape[0]
+    C = max(int(math.floor(cf * k * T / E)), k)
+    logits = x @ inp["W_router"].astype(np.float64).T
+    ex = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    s = p if inp["router_bias"] is None else (p + inp["router_bias"]).astype(np.float32)
+    idx = np.array([sorted(range(E), key=lambda e: (-float(s[t, e]), e))[:k] for t in range(T)])
+    final = brute_next_best(idx, s, E, C)
+    y = np.zeros((T, d))
+    for t in range(T):
+        tot = sum(float(p[t, e]) for e in idx[t])
+        for j in range(k):
+            e = int(final[t, j])
+            if e < 0:
+                continue
+            w = np.float32(float(p[t, idx[t, j]]) / tot)
+            g = inp["W_gate"][e].astype(np.float64) @ x[t]
+            u = inp["W_up"][e].astype(np.float64) @ x[t]
+            h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+            if h_bf16:
+                h = oracle.bf16_round(h)
+            o = (inp["W_down"][e].astype(np.float64) @ h.astype(np.float64)).astype(np.float32)
+            y[t] += float(w) * o.astype(np.float64)
+    return y.astype(np.float32)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,cf,bias,hb", [
+    (40, 16, 6, 2, 20, 1.0, 0.0, False),
+    (48, 12, 8, 1, 8, 1.25, 0.2, True),
+    (36, 16, 5, 3, 12, 0.8, 0.05, True),
+])
+def test_next_best_forward_matches_per_token_loop(T, d, E, k, F, cf, bias, hb):
+    inp = make_small(T, d, E, k, F, 0, seed=7 * T + d, bias=bias)
+    out = oracle.forward(inp, k, cf, 0, h_bf16=hb, next_best=True)
+    ref = per_token_next_best(inp, k, cf, hb)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-5, atol=1e-6)
+    # forward_rows follows the redirected experts too
+    rows = np.arange(0, T, 3)
+    yr = oracle.forward_rows(inp, rows, k, cf, 0, h_bf16=hb, routing=out["route"],
+                             disp=out["dispatch"])
+    np.testing.assert_allclose(yr, out["y"][rows], rtol=1e-5, atol=1e-6)
+
+
+def test_next_best_planted_mistakes_are_caught(monkeypatch):
+    """Offering the overflow to the token's k-th instead of (k+1)-th best expert, taking
+    offers last-come first, or ignoring the capacity fails a pin."""
+    orig = mo.next_best_candidates
+    with monkeypatch.context() as m:
+        m.setattr(mo, "next_best_candidates",
+                  lambda s, k, idx=None: np.roll(orig(s, k, idx), 1, axis=1))
+        m.setattr(oracle, "next_best_candidates", mo.next_best_candidates)
+        assert _pins_fail(test_next_best_hand_example) or _pins_fail(
+            lambda: test_next_best_matches_sequential_loop(50, 16, 4, 14, 4))
+    orig_d = mo.dispatch_next_best
+    with monkeypatch.context() as m:
+        def last_come(idx, cand, E, C):
+            T, k = idx.shape
+            d = orig_d(idx[::-1].copy(), np.asarray(cand)[::-1].copy(), E, C)
+            ex = d["expert"].reshape(T, k)[::-1].reshape(-1)
+            return dict(d, expert=ex)
+        m.setattr(mo, "dispatch_next_best", last_come)
+        m.setattr(oracle, "dispatch_next_best", mo.dispatch_next_best)
+        assert _pins_fail(lambda: test_next_best_matches_sequential_loop(40, 6, 2, 9, 0))
+    with monkeypatch.context() as m:
+        m.setattr(mo, "dispatch_next_best",
+                  lambda idx, cand, E, C: orig_d(idx, cand, E, 10 ** 9) if C else None)
+        m.setattr(oracle, "dispatch_next_best", mo.dispatch_next_best)
+        assert _pins_fail(test_next_best_hand_example)
