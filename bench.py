@@ -27,7 +27,8 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 # Which roof bounds the dominant (gate/up) kernel for each workload.
 BOUND = {"mixtral_prefill": "mfma", "fine_grained_shared": "mfma", "mixtral_decode": "hbm",
          "switch_capacity": "hbm", "tiny_f32": "alu", "mixtral_decode_fp8": "hbm",
-         "switch_capacity_fp8": "hbm", "mixtral_prefill_ec": "mfma"}
+         "switch_capacity_fp8": "hbm", "mixtral_prefill_ec": "mfma",
+         "switch_capacity_nb": "hbm"}
 
 
 def log(*a):
@@ -76,6 +77,7 @@ def main():
     T, d, E, k, F, S = wl.T, wl.d, wl.E, wl.k, wl.F, wl.n_shared
     fp8 = wl.weights == "fp8"     # e4m3 expert weights with per-row scales
     ec = wl.routing == "expert"   # expert-choice routing: each expert takes its top-C tokens
+    nb = wl.routing == "next_best"   # capacity overflow handed to the next-best expert
     out_dtype = wl.torch_dtype
     desc = moe.make_desc(T, d, E, F, k, S, wl.capacity_factor, wl.torch_dtype, out_dtype)
     ws = moe.alloc_workspace_expert_choice(desc, dev) if ec else moe.alloc_workspace(desc, dev)
@@ -91,6 +93,11 @@ def main():
         fwd_fn = L.moe_forward_expert_choice
         fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["W_gate"]),
                     P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p), P(ws), ws.numel(), sp)
+    elif nb:
+        fwd_fn = L.moe_forward_next_best
+        fwd_args = (dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]),
+                    P(dinp["W_gate"]), P(dinp["W_up"]), P(dinp["W_down"]), P(out), P(f), P(p),
+                    P(ws), ws.numel(), sp)
     elif fp8:
         W8 = [P(dinp[n]) for n in ("Wq_gate", "Wq_up", "Wq_down", "s_gate", "s_up", "s_down")]
         fwd_fn = L.moe_forward_fp8
@@ -154,6 +161,14 @@ def main():
     if ec:   # the expert-choice layer's own stages
         calls = expert_choice_stages(moe, L, desc, dinp, ws, out2, f, p, P, sp, dev)
         counts, offsets = calls.counts, calls.offsets
+    if nb:   # route with the candidates, dispatch with the redirect round
+        cand = torch.empty(T, k, dtype=torch.int32, device=dev)
+        calls[0] = ("route", lambda: L.moe_route_next_best(
+            dref, P(dinp["x"]), P(dinp["W_router"]), P(dinp["router_bias"]), P(idx), P(w),
+            P(cand), P(f), P(p), P(ws), ws.numel(), sp))
+        calls[1] = ("dispatch", lambda: L.moe_dispatch_next_best(
+            dref, P(idx), P(cand), P(counts), P(offsets), P(perm), P(slot), P(ws), ws.numel(),
+            sp))
     for _ in range(max(1, args.warmup)):
         for name, c in calls:
             if c():
@@ -240,7 +255,8 @@ def main():
                    "selection_bias": wl.bias_range > 0, "out_dtype": str(out_dtype).split(".")[-1],
                    "expert_weights": "e4m3 + f32 per-row scale" if fp8 else wl.dtype,
                    "routing": "expert choice (top-C tokens per expert)" if ec
-                              else "token choice (top-k experts per token)"},
+                              else "token choice, capacity overflow to the next-best expert"
+                              if nb else "token choice (top-k experts per token)"},
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,

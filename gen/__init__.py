@@ -53,7 +53,8 @@ class Workload:
     bias_range: float = 0.0           # > 0: selection bias ~ U(-r, r)
     row_scales: tuple | None = None   # per-expert router row scale (load skew)
     weights: str = "same"             # "same" (as dtype) or "fp8": e4m3 expert weights
-    routing: str = "token"            # "token" (top-k per token) or "expert" (top-C per expert)
+    routing: str = "token"            # "token" (top-k per token), "next_best" (top-k, capacity
+                                      # overflow redirected) or "expert" (top-C per expert)
     recipe: str = ""
 
     def replace(self, **kw) -> "Workload":
@@ -99,6 +100,11 @@ WORKLOADS["mixtral_decode_fp8"] = WORKLOADS["mixtral_decode"].replace(
 WORKLOADS["switch_capacity_fp8"] = WORKLOADS["switch_capacity"].replace(
     name="switch_capacity_fp8", weights="fp8",
     recipe=WORKLOADS["switch_capacity"].recipe + "; expert weights e4m3 with per-row scales")
+# The Switch layer's inputs with the capacity overflow handed to the next-best expert.
+WORKLOADS["switch_capacity_nb"] = WORKLOADS["switch_capacity"].replace(
+    name="switch_capacity_nb", routing="next_best",
+    recipe=WORKLOADS["switch_capacity"].recipe + "; overflow redirected to each token's "
+    "next-best expert (one round)")
 # The prefill layer's inputs (same seeds, same values) under expert-choice routing: each
 # expert takes C = T k / E = 1024 tokens.
 WORKLOADS["mixtral_prefill_ec"] = WORKLOADS["mixtral_prefill"].replace(

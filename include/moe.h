@@ -211,6 +211,33 @@ moe_status_t moe_experts_down_fp8(const moe_desc_t* desc, const void* H, const i
 moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t* slot_pos,
                          const float* topk_w, void* out, void* stream);
 
+/* ---- Capacity overflow to the next-best expert ("Chapter 30", 30.5.2: tokens past an
+ * expert's capacity are dropped or handed to the next-best expert).  One redirect round:
+ * round 0 is the capacity cut of moe_dispatch (each expert keeps its first C assignments
+ * in row-major (token, slot) order); the m-th assignment of token t dropped there (slot
+ * order) is offered to cand[t, m], the token's (k+1+m)-th best expert by selection score
+ * (ties to the lower index; -1 past E); every expert takes the offers in row-major order
+ * while its rows stay within C; the rest are dropped.  An expert's rows are its round-0
+ * assignments, then its accepted offers, each in row-major order.  A redirected slot keeps
+ * its weight topk_w[t, j]; the combine is moe_combine.  f and P are those of moe_forward.
+ * capacity_factor must be > 0 (else MOE_E_SHAPE).  Workspace: moe_workspace_bytes.
+ *   moe_route_next_best    moe_route plus cand [T, k] int32
+ *   moe_dispatch_next_best moe_dispatch with the redirect (counts = the top-k histogram)
+ *   moe_forward_next_best  the whole layer (arguments as moe_forward) */
+moe_status_t moe_forward_next_best(const moe_desc_t* desc, const void* x, const void* W_router,
+                                   const float* router_bias, const void* W_gate,
+                                   const void* W_up, const void* W_down, void* out, float* f,
+                                   float* p, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+moe_status_t moe_route_next_best(const moe_desc_t* desc, const void* x, const void* W_router,
+                                 const float* router_bias, int32_t* topk_idx, float* topk_w,
+                                 int32_t* cand, float* f, float* p, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+moe_status_t moe_dispatch_next_best(const moe_desc_t* desc, const int32_t* topk_idx,
+                                    const int32_t* cand, int32_t* counts, int32_t* offsets,
+                                    int32_t* perm_src, int32_t* slot_pos, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* ---- Expert-choice routing ("Mixture of Experts (MoE) memo", routing section: the
  * expert-choice row of the routing-design table, every expert picks the tokens that suit
  * it and loads come out equal; "Mixture-of-experts in practice", top-k section: each

@@ -291,7 +291,8 @@ def expert_weights(inputs: dict, e: int):
 
 
 def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
-            h_bf16: bool = True, idx_override=None, next_best: bool = False) -> dict:
+            h_bf16: bool = True, idx_override=None, next_best: bool = False,
+            cand_override=None) -> dict:
     """The whole layer: route -> stats -> dispatch -> grouped experts -> combine.
 
     ``inputs`` holds x, W_router, router_bias (or None), W_gate, W_up, W_down as torch
@@ -299,7 +300,8 @@ def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 
     near-tied tokens have more than one correct routing); the weights are then
     renormalised from the same unbiased probabilities.  ``next_best`` hands assignments
     that overflow an expert's capacity to their token's next-best experts
-    (``dispatch_next_best``) instead of dropping them.
+    (``dispatch_next_best``) instead of dropping them; ``cand_override`` replaces their
+    candidates (near-tied scores).
     """
     x = _np(inputs["x"])
     Wr = _np(inputs["W_router"])
@@ -313,7 +315,8 @@ def forward(inputs: dict, k: int, capacity_factor: float = 0.0, n_shared: int = 
     f, P = aux_stats(r["p"], r["idx"], E)
     C = capacity(T, k, E, capacity_factor)
     if next_best:
-        r["cand"] = next_best_candidates(r["s"], k, r["idx"])
+        r["cand"] = (next_best_candidates(r["s"], k, r["idx"]) if cand_override is None
+                     else np.asarray(cand_override, np.int32))
         disp = dispatch_next_best(r["idx"], r["cand"], E, C)
     else:
         disp = dispatch(r["idx"], E, C)

@@ -8,6 +8,8 @@ kernels.  The functions mirror the C entry points:
     route(...), dispatch(...), experts(...), combine(...)
     forward_fp8(...) and the *_fp8 stages (8-bit expert weights)
     forward_expert_choice(...), route_expert_choice(...), combine_expert_choice(...)
+    forward_next_best(...), route_next_best(...), dispatch_next_best(...) (capacity
+    overflow handed to the next-best expert)
 
 There is no fallback: without the built library (python -m
 sparse_mixture_experts_24_amd.build) every call raises.
@@ -31,7 +33,8 @@ EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_capacit
            "moe_experts_down", "moe_combine", "moe_forward_fp8", "moe_experts_fp8",
            "moe_experts_gate_up_fp8", "moe_experts_down_fp8",
            "moe_workspace_bytes_expert_choice", "moe_capacity_expert_choice",
-           "moe_route_expert_choice", "moe_combine_expert_choice", "moe_forward_expert_choice")
+           "moe_route_expert_choice", "moe_combine_expert_choice", "moe_forward_expert_choice",
+           "moe_forward_next_best", "moe_route_next_best", "moe_dispatch_next_best")
 
 
 class MoeDesc(ctypes.Structure):
@@ -103,6 +106,12 @@ def lib():
         L.moe_combine_expert_choice.argtypes = [D, P, P, P, P, P]
         L.moe_forward_expert_choice.restype = I
         L.moe_forward_expert_choice.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_forward_next_best.restype = I
+        L.moe_forward_next_best.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_route_next_best.restype = I
+        L.moe_route_next_best.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.moe_dispatch_next_best.restype = I
+        L.moe_dispatch_next_best.argtypes = [D, P, P, P, P, P, P, P, S, P]
         _lib = L
     return _lib
 
@@ -505,3 +514,75 @@ def combine_expert_choice(Yp, slot, probs, d, k, capacity_factor, n_shared=0,
                                          _ptr(out), _stream(dev))
     _check("moe_combine_expert_choice", st)
     return out
+
+
+# ----------------------------------------------------------------------------- next best
+def forward_next_best(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor,
+                      out=None, f=None, p=None, out_dtype=None, workspace=None):
+    """The layer with capacity overflow handed to each token's next-best experts instead
+    of dropped.  Returns (y, f, p)."""
+    dev = x.device
+    desc = desc_for(x, W_router, W_gate, k, capacity_factor, out_dtype)
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = W_gate.shape
+    for t, n, shp in ((x, "x", (T, d)), (W_router, "W_router", (E, d)),
+                      (W_gate, "W_gate", (G, F, d)), (W_up, "W_up", (G, F, d)),
+                      (W_down, "W_down", (G, d, F))):
+        _require(t, n, dev, x.dtype, shp)
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    odt = out_dtype or x.dtype
+    out = torch.empty(T, d, dtype=odt, device=dev) if out is None else out
+    f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+    p = torch.empty(E, dtype=torch.float32, device=dev) if p is None else p
+    _require(out, "out", dev, odt, (T, d))
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_forward_next_best(ctypes.byref(desc), _ptr(x), _ptr(W_router),
+                                     _ptr(router_bias), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+                                     _ptr(out), _ptr(f), _ptr(p), _ptr(ws), ws.numel(),
+                                     _stream(dev))
+    _check("moe_forward_next_best", st)
+    return out, f, p
+
+
+def route_next_best(x, W_router, router_bias, k, workspace=None):
+    """Router + top-k + the next-best candidates.  Returns (topk_idx, topk_w, cand, f, p)."""
+    dev = x.device
+    T, d = x.shape
+    E = W_router.shape[0]
+    desc = make_desc(T, d, E, 64, k, 0, 0.0, x.dtype)
+    _require(x, "x", dev)
+    _require(W_router, "W_router", dev, x.dtype, (E, d))
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    cand = torch.empty(T, k, dtype=torch.int32, device=dev)
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    p = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_route_next_best(ctypes.byref(desc), _ptr(x), _ptr(W_router), _ptr(router_bias),
+                                   _ptr(idx), _ptr(w), _ptr(cand), _ptr(f), _ptr(p), _ptr(ws),
+                                   ws.numel(), _stream(dev))
+    _check("moe_route_next_best", st)
+    return idx, w, cand, f, p
+
+
+def dispatch_next_best(topk_idx, cand, n_experts, capacity_factor, workspace=None):
+    """Dispatch with the capacity overflow offered to the candidates.  Returns (counts,
+    offsets, perm_src, slot_pos)."""
+    dev = topk_idx.device
+    T, k = topk_idx.shape
+    E = int(n_experts)
+    desc = make_desc(T, 64, E, 64, k, 0, capacity_factor, torch.bfloat16)
+    _require(topk_idx, "topk_idx", dev, torch.int32, (T, k))
+    _require(cand, "cand", dev, torch.int32, (T, k))
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = _ws(desc, dev, workspace)
+    st = lib().moe_dispatch_next_best(ctypes.byref(desc), _ptr(topk_idx), _ptr(cand), _ptr(counts),
+                                      _ptr(offsets), _ptr(perm), _ptr(slot), _ptr(ws), ws.numel(),
+                                      _stream(dev))
+    _check("moe_dispatch_next_best", st)
+    return counts, offsets, perm, slot

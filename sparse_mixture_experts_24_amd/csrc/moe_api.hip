@@ -55,6 +55,9 @@ Workspace carve_workspace(const moe_desc_t& d, void* base) {
   w.offsets = (int32_t*)take((E + 1) * 4);
   w.perm_src = (int32_t*)take(TK * 4);
   w.slot_pos = (int32_t*)take(TK * 4);
+  w.cand = (int32_t*)take(TK * 4);
+  w.offer = (int32_t*)take(TK * 4);
+  w.ocounts = (int32_t*)take(E * 4);
   w.H = take((size_t)rows * d.d_ff * esz);
   w.Yp = (float*)take((size_t)rows * d.d_model * 4);
   w.bytes = off;   // the minimum; monotone in T
@@ -173,13 +176,33 @@ static moe_status_t down_impl(const moe_desc_t* desc, const void* H, const int32
   return MOE_OK;
 }
 
+// Round-0 ranks (from the block histograms in blk, chunked by chunk), offers to the
+// next-best candidates, and the final placement: offsets, perm_src, slot_pos.
+static hipError_t dispatch_next_best(const moe_desc_t& d, const int32_t* topk_idx,
+                                     const int32_t* cand, int chunk, int32_t* blk,
+                                     const int32_t* counts, const Workspace& w,
+                                     int32_t* offsets, int32_t* perm_src, int32_t* slot_pos,
+                                     hipStream_t s) {
+  const int64_t TK = d.T * d.top_k, C = capacity_of(d);
+  const int E = (int)d.n_experts, k = (int)d.top_k;
+  hipError_t e;
+  if ((e = launch_ranks(topk_idx, TK, E, chunk, blk, slot_pos, s)) != hipSuccess) return e;
+  if ((e = launch_offers(slot_pos, cand, d.T, k, E, C, w.offer, blk, s)) != hipSuccess) return e;
+  if ((e = launch_expert_scan(blk, ceil_div(TK, kDispatchChunk), E, nullptr, d.T, k, w.ocounts,
+                              nullptr, nullptr, nullptr, 0, s)) != hipSuccess)
+    return e;
+  return launch_place_next_best(topk_idx, w.offer, TK, E, C, counts, w.ocounts, blk, offsets,
+                                perm_src, slot_pos, s);
+}
+
 static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const void* W_router,
                                  const float* router_bias, const ExpertWeights& ew, void* out,
                                  float* f, float* p, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 void* stream, bool next_best = false) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_desc_t& d = *desc;
+  if (next_best && !(d.capacity_factor > 0.0f)) return MOE_E_SHAPE;
   if (!W_router || !ew.gate || !ew.up || !ew.down || (d.T > 0 && (!x || !out)))
     return MOE_E_NULL;
   if ((st = check_fp8(d, ew)) != MOE_OK) return st;
@@ -195,11 +218,15 @@ static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const vo
   const int64_t C = capacity_of(d);
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
   MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, nullptr,
-                       w.p_part, w.cnt_part, s));
+                       next_best ? w.cand : nullptr, w.p_part, w.cnt_part, s));
   MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
                              f, p, w.ctr, kTileCounters, s));
-  MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
-                         w.perm_src, w.slot_pos, s));
+  if (next_best)
+    MOE_HIP(dispatch_next_best(d, w.topk_idx, w.cand, chunk, w.cnt_part, w.counts, w, w.offsets,
+                               w.perm_src, w.slot_pos, s));
+  else
+    MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
+                           w.perm_src, w.slot_pos, s));
   const GemmRows rows = token_choice_rows(d);
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
   MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
@@ -313,8 +340,8 @@ moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* W_rout
   if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const RoutePlan rp = route_plan(d);
-  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, gap, nullptr, w.p_part,
-                       w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, gap, nullptr, nullptr,
+                       w.p_part, w.cnt_part, s));
   if (f || p)
     MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
                                (int)d.top_k, w.counts, f, p, nullptr, 0, s));
@@ -458,8 +485,8 @@ moe_status_t moe_route_expert_choice(const moe_desc_t* desc, const void* x,
                                  nullptr, 0, s));
     return MOE_OK;
   }
-  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, probs, w.p_part,
-                       w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, probs, nullptr,
+                       w.p_part, w.cnt_part, s));
   if (p)
     MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k,
                                w.counts, nullptr, p, nullptr, 0, s));
@@ -506,8 +533,8 @@ moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
                                  nullptr, 0, s));
     return MOE_OK;
   }
-  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, w.probs, w.p_part,
-                       w.cnt_part, s));
+  MOE_HIP(launch_route(d, x, W_router, nullptr, nullptr, nullptr, nullptr, w.probs, nullptr,
+                       w.p_part, w.cnt_part, s));
   // P from the route blocks' partial sums; also clears the GEMMs' work counters
   MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
                              nullptr, p, w.ctr, kTileCounters, s));
@@ -516,6 +543,64 @@ moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
   MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
   MOE_HIP(launch_ec_combine(d, rows.routed, w.Yp, w.Yp2, w.slot, w.probs, out, s));
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- capacity overflow to the next-best expert
+extern "C" {
+
+moe_status_t moe_forward_next_best(const moe_desc_t* desc, const void* x, const void* W_router,
+                                   const float* router_bias, const void* W_gate,
+                                   const void* W_up, const void* W_down, void* out, float* f,
+                                   float* p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return forward_impl(desc, x, W_router, router_bias, plain_weights(W_gate, W_up, W_down), out,
+                      f, p, workspace, workspace_bytes, stream, true);
+}
+
+moe_status_t moe_route_next_best(const moe_desc_t* desc, const void* x, const void* W_router,
+                                 const float* router_bias, int32_t* topk_idx, float* topk_w,
+                                 int32_t* cand, float* f, float* p, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!W_router || (d.T > 0 && (!x || !topk_idx || !topk_w || !cand))) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(W_router)) return MOE_E_UNSUPPORTED;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RoutePlan rp = route_plan(d);
+  MOE_HIP(launch_route(d, x, W_router, router_bias, topk_idx, topk_w, nullptr, nullptr, cand,
+                       w.p_part, w.cnt_part, s));
+  if (f || p)
+    MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, (int)d.n_experts, w.p_part, d.T,
+                               (int)d.top_k, w.counts, f, p, nullptr, 0, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch_next_best(const moe_desc_t* desc, const int32_t* topk_idx,
+                                    const int32_t* cand, int32_t* counts, int32_t* offsets,
+                                    int32_t* perm_src, int32_t* slot_pos, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc_t& d = *desc;
+  if (!(d.capacity_factor > 0.0f)) return MOE_E_SHAPE;
+  if (!counts || !offsets || (d.T > 0 && (!topk_idx || !cand || !perm_src || !slot_pos)))
+    return MOE_E_NULL;
+  Workspace w;
+  if ((st = check_ws(d, workspace, workspace_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t TK = d.T * d.top_k;
+  const int E = (int)d.n_experts;
+  MOE_HIP(launch_hist(topk_idx, TK, E, kDispatchChunk, w.cnt_part, s));
+  MOE_HIP(launch_expert_scan(w.cnt_part, ceil_div(TK, kDispatchChunk), E, nullptr, d.T,
+                             (int)d.top_k, counts, nullptr, nullptr, nullptr, 0, s));
+  MOE_HIP(dispatch_next_best(d, topk_idx, cand, kDispatchChunk, w.cnt_part, counts, w, offsets,
+                             perm_src, slot_pos, s));
   return MOE_OK;
 }
 

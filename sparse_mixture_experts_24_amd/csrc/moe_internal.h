@@ -48,6 +48,9 @@ struct Workspace {
   void* H;             // [T*k + S*T, F] dtype
   float* Yp;           // [T*k + S*T, d]
   int32_t* ctr;        // kTileCounters work counters of the grouped GEMMs
+  int32_t* cand;       // [T*k] next-best candidates (overflow redirect)
+  int32_t* offer;      // [T*k] expert offered each dropped assignment, or -1
+  int32_t* ocounts;    // [E] offers per expert
   float* Yp2;          // second partial of the split down GEMM, or NULL
   size_t bytes;        // minimum size (without Yp2)
   size_t bytes_full;   // with Yp2 when the layer splits its down GEMM
@@ -78,10 +81,12 @@ constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe
 // ---------------------------------------------------------------- launchers
 // gap (optional, [T]): s_(k) - s_(k+1) of each token's selection scores (+inf if k == E).
 // probs (optional, [T, E]): the router probabilities.  With topk_idx NULL no top-k is
-// taken (and the block histograms stay zero).
+// taken (and the block histograms stay zero).  cand (optional, [T, k]): the experts
+// ranked k+1 .. 2k by selection score, -1 past E.
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
-                        float* probs, float* p_part, int32_t* cnt_part, hipStream_t s);
+                        float* probs, int32_t* cand, float* p_part, int32_t* cnt_part,
+                        hipStream_t s);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
 // zero (optional): nzero <= 256 int32 that block 0 also sets to zero.
@@ -91,6 +96,20 @@ hipError_t launch_expert_scan(int32_t* blk, int64_t nb, int E, const float* p_pa
 hipError_t launch_scatter(const int32_t* idx, int64_t NA, int E, int chunk, int64_t C,
                           const int32_t* blk_base, const int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
+// Overflow to the next-best expert (C >= 0), after hist + expert_scan of topk_idx:
+//  ranks   rank0[i] = stable rank of assignment i within its top-k expert
+//  offers  offer[i] = cand[t, m] for the m-th assignment of token t with rank0 >= C (-1
+//          otherwise), and the block histograms of the offers (chunk kDispatchChunk)
+//  place   (after expert_scan of those histograms -> ocounts) offsets of kept0 + accepted
+//          offers, and the final slot_pos / perm_src.  rank0 may live in slot_pos.
+hipError_t launch_ranks(const int32_t* idx, int64_t NA, int E, int chunk,
+                        const int32_t* blk_base, int32_t* rank0, hipStream_t s);
+hipError_t launch_offers(const int32_t* rank0, const int32_t* cand, int64_t T, int k, int E,
+                         int64_t C, int32_t* offer, int32_t* blk, hipStream_t s);
+hipError_t launch_place_next_best(const int32_t* idx, const int32_t* offer, int64_t NA, int E,
+                                  int64_t C, const int32_t* counts, const int32_t* ocounts,
+                                  const int32_t* offer_base, int32_t* offsets,
+                                  int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
 // Expert weights as the grouped GEMMs take them: tensors of desc.dtype, or (fp8 set, bf16
 // layers only) e4m3 codes with one float32 scale per output row.
 struct ExpertWeights {

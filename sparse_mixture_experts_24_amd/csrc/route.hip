@@ -100,12 +100,14 @@ __device__ inline void wave_argmax(float& v, int& e) {
 // Softmax + top-k + renorm for the tokens of one block, logits in LDS rows of E_PAD.
 // Waves take tokens tt = wave, wave + 4, ...  Accumulates p into psum (per lane, expert
 // lane + 64 i) and the chosen experts into the LDS histogram cnt.  probs (optional)
-// receives every p; k = 0 takes no top-k.
+// receives every p; k = 0 takes no top-k.  cand (optional, [T, k]) receives the experts
+// ranked k+1 .. 2k by selection score (-1 past E).
 template <int E_PAD>
 __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E, int k,
                                   const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
                                   float* __restrict__ topk_w, float* __restrict__ gap,
-                                  float* __restrict__ probs, float* psum, int* cnt) {
+                                  float* __restrict__ probs, int32_t* __restrict__ cand,
+                                  float* psum, int* cnt) {
   constexpr int NV = (E_PAD + 63) / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bv[NV];
@@ -146,10 +148,12 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
       if (probs != nullptr && e < E) probs[(size_t)t * E + e] = v[i];
     }
     unsigned taken = 0;
-    int my_idx = 0;
+    int my_idx = 0, my_cand = -1;
     float my_p = 0.0f, s_k = 0.0f, tot = 0.0f;
-    // k rounds of wavefront argmax (one more, not taken, when the gap is asked for)
-    const int rounds = k + (gap != nullptr ? 1 : 0);
+    // k rounds of wavefront argmax, then the candidates (extra rounds) and/or one more
+    // for the gap
+    const int extra = cand != nullptr ? min(k, E - k) : 0;
+    const int rounds = k + max(extra, gap != nullptr ? 1 : 0);
     for (int r = 0; r < rounds; ++r) {
       float bvv = -INFINITY;
       int be = 0x7fffffff;
@@ -162,9 +166,14 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
         }
       }
       wave_argmax(bvv, be);
-      if (r == k) {            // gap = s_(k) - s_(k+1); +inf when k == E
-        if (lane == 0) gap[t] = s_k - bvv;
-        break;
+      if (r >= k) {
+        if (r == k && gap != nullptr && lane == 0) gap[t] = s_k - bvv;   // +inf when k == E
+        if (r - k < extra) {   // candidate r - k: the (r+1)-th best expert
+          const bool ok = be < E;
+          if (ok && lane == (be & 63)) taken |= 1u << (be >> 6);
+          if (lane == r - k) my_cand = ok ? be : -1;
+        }
+        continue;
       }
       s_k = bvv;
       const bool ok = be < E;   // always true for finite inputs and k <= E
@@ -185,6 +194,7 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
     if (lane < k) {
       topk_idx[(size_t)t * k + lane] = my_idx;
       topk_w[(size_t)t * k + lane] = my_p / tot;
+      if (cand != nullptr) cand[(size_t)t * k + lane] = lane < extra ? my_cand : -1;
     }
   }
 }
@@ -210,8 +220,8 @@ template <int EPW, int TPW, int KS, int R>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ gap, float* __restrict__ probs, float* __restrict__ p_part,
-    int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ probs, int32_t* __restrict__ cand,
+    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
   constexpr int EW = 4 / KS;
   constexpr int E_PAD = 16 * EPW * EW;
   constexpr int BT = 16 * TPW;
@@ -314,8 +324,8 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, psum,
-                    cnt);
+  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, cand,
+                    psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -325,8 +335,8 @@ template <int E_PAD>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ gap, float* __restrict__ probs, float* __restrict__ p_part,
-    int32_t* __restrict__ cnt_part) {
+    float* __restrict__ gap, float* __restrict__ probs, int32_t* __restrict__ cand,
+    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
   constexpr int BT = 16;
   constexpr int NV = (E_PAD + 63) / 64;
   __shared__ float lg[BT][E_PAD];
@@ -353,7 +363,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, psum, cnt);
+  route_tail<E_PAD>(&lg[0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, cand, psum,
+                    cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
@@ -394,7 +405,8 @@ RoutePlan route_plan(const moe_desc_t& d) {
 
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
-                        float* probs, float* p_part, int32_t* cnt_part, hipStream_t s) {
+                        float* probs, int32_t* cand, float* p_part, int32_t* cnt_part,
+                        hipStream_t s) {
   const RoutePlan rp = route_plan(d);
   if (rp.n_blocks == 0) return hipSuccess;
   const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts;
@@ -406,7 +418,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
 #define MOE_ROUTE_F32(EP)                                                                     \
   if (rp.E_pad == EP) {                                                                       \
     hipLaunchKernelGGL(route_f32_kernel<EP>, grid, block, 0, s, xx, ww, bias, T, dm, E, k,    \
-                       topk_idx, topk_w, gap, probs, p_part, cnt_part);                       \
+                       topk_idx, topk_w, gap, probs, cand, p_part, cnt_part);                 \
     return hipGetLastError();                                                                 \
   }
     MOE_ROUTE_F32(64)
@@ -424,7 +436,8 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
     constexpr int R_ = (EPW_ + TPW_) <= 3 ? 8 : 200 / (8 * (EPW_ + TPW_));                      \
     hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, R_>), grid, block, 0, s, xx, ww,   \
-                       bias, T, dm, E, k, topk_idx, topk_w, gap, probs, p_part, cnt_part);    \
+                       bias, T, dm, E, k, topk_idx, topk_w, gap, probs, cand, p_part,         \
+                       cnt_part);                                                             \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTE_BF16(1, 1, 4)

@@ -270,3 +270,32 @@ def expert_choice_rows_reference(inp, rows, sel, probs, n_shared, h_bf16):
     for i, wt, e, pos, parts, o, xr, W in items:
         y[i] += wt * o[0].astype(np.float64)
     return y.astype(np.float32), items
+
+
+def check_candidates(cand_gpu, idx_gpu, s_ref, k):
+    """The next-best candidates: bit-exact for tokens whose remaining selection scores
+    (outside the chosen k) are separated by >= 1e-6 among the first min(k, E-k)+1; else
+    they must still be the best-scored remaining experts within 1e-6, in descending
+    order.  Entries past E - k are -1."""
+    cand_gpu = np.asarray(cand_gpu, np.int64)
+    idx_gpu = np.asarray(idx_gpu, np.int64)
+    T, E = s_ref.shape
+    m = min(k, E - k)
+    assert np.all(cand_gpu[:, m:] == -1)
+    exp = oracle.next_best_candidates(s_ref, k, idx_gpu)
+    s2 = s_ref.astype(np.float64).copy()
+    np.put_along_axis(s2, idx_gpu, -np.inf, axis=1)
+    srt = -np.sort(-s2, axis=1)[:, :E - k]
+    q = min(m + 1, E - k)
+    gaps = (srt[:, :q - 1] - srt[:, 1:q]).min(axis=1) if q >= 2 else np.full(T, np.inf)
+    sure = gaps >= NEAR_TIE
+    bad = np.nonzero(np.any(cand_gpu[sure, :m] != exp[sure, :m], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} tokens with other candidates"
+    for t in np.nonzero(~sure)[0]:
+        c = cand_gpu[t, :m]
+        assert len(set(c.tolist())) == m and not set(c.tolist()) & set(idx_gpu[t].tolist())
+        sc = s2[t, c]
+        assert np.all(np.diff(sc) <= NEAR_TIE)
+        rest = np.delete(s2[t], np.concatenate([idx_gpu[t], c]))
+        assert rest.size == 0 or sc.min() >= rest.max() - NEAR_TIE
+    return ~sure

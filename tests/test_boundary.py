@@ -178,3 +178,20 @@ def test_expert_choice_validation_and_capacity(L):
                                      None, fake, need, None) == 1
     assert L.moe_combine_expert_choice(ctypes.byref(d), fake, None, fake, fake, None) == 1
     assert L.moe_combine_expert_choice(ctypes.byref(desc()), fake, fake, fake, fake, None) == 2
+
+
+def test_next_best_entry_points_validate_on_the_host(L):
+    d = desc(capacity_factor=1.25)
+    need = L.moe_workspace_bytes(ctypes.byref(d))
+    fake = ctypes.c_void_p(0x100000)
+    nocap = desc(capacity_factor=0.0)
+    args = (fake, fake, None, fake, fake, fake, fake, None, None, fake, need, None)
+    assert L.moe_forward_next_best(ctypes.byref(nocap), *args) == 2
+    assert L.moe_dispatch_next_best(ctypes.byref(nocap), fake, fake, fake, fake, fake, fake, fake,
+                                    need, None) == 2
+    assert L.moe_forward_next_best(ctypes.byref(d), None, *args[1:]) == 1
+    assert L.moe_forward_next_best(ctypes.byref(d), *args[:-3], fake, need // 4, None) == 4
+    assert L.moe_route_next_best(ctypes.byref(d), fake, fake, None, fake, fake, None, None, None,
+                                 fake, need, None) == 1
+    assert L.moe_dispatch_next_best(ctypes.byref(d), fake, None, fake, fake, fake, fake, fake,
+                                    need, None) == 1
