@@ -199,6 +199,135 @@ __device__ inline void route_tail(const float* lg, int BT, int t0, int T, int E,
   }
 }
 
+// Reductions over one token's segment of SEG = 16 or 32 lanes (DPP inside a row, then a
+// permlane16 swap to join the two rows of a 32-lane segment); every lane of the segment
+// ends with the same bits.
+template <int SEG, class Op>
+__device__ inline float seg_reduce(float v, Op op) {
+  v = op(v, dpp_f<DPP_QUAD_1032>(v));
+  v = op(v, dpp_f<DPP_QUAD_2301>(v));
+  v = op(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = op(v, dpp_f<DPP_MIRROR>(v));
+  if constexpr (SEG == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
+// (v, e, p) <- the better candidate (larger v, then lower e), p travelling with it.
+template <int CTRL>
+__device__ inline void seg_argmax_step(float& v, int& e, float& p) {
+  const float ov = dpp_f<CTRL>(v), op_ = dpp_f<CTRL>(p);
+  const int oe = dpp_i<CTRL>(e);
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+    p = op_;
+  }
+}
+template <int SEG>
+__device__ inline void seg_argmax(float& v, int& e, float& p) {
+  seg_argmax_step<DPP_QUAD_1032>(v, e, p);
+  seg_argmax_step<DPP_QUAD_2301>(v, e, p);
+  seg_argmax_step<DPP_HALF_MIRROR>(v, e, p);
+  seg_argmax_step<DPP_MIRROR>(v, e, p);
+  if constexpr (SEG == 32) {
+    const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+    const auto re = __builtin_amdgcn_permlane16_swap((unsigned)e, (unsigned)e, false, false);
+    const auto rp = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p),
+                                                     false, false);
+    v = __uint_as_float(rv[0]);
+    e = (int)re[0];
+    p = __uint_as_float(rp[0]);
+    const float ov = __uint_as_float(rv[1]);
+    const int oe = (int)re[1];
+    if (ov > v || (ov == v && oe < e)) {
+      v = ov;
+      e = oe;
+      p = __uint_as_float(rp[1]);
+    }
+  }
+}
+
+// route_tail for E_PAD <= 32: a wave takes 64 / E_PAD tokens at once, one segment of
+// E_PAD lanes per token (lane = expert), so the reductions of several tokens run side by
+// side instead of one token after the other.  Same results as route_tail (the sums of p
+// and of the chosen p run over the same values; only their order within a segment
+// differs) and the same outputs.
+template <int E_PAD>
+__device__ inline void route_tail_packed(const float* lg, int BT, int t0, int T, int E, int k,
+                                         const float* __restrict__ bias,
+                                         int32_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_w, float* __restrict__ gap,
+                                         float* __restrict__ probs, int32_t* __restrict__ cand,
+                                         float* psum, int* cnt) {
+  static_assert(E_PAD == 16 || E_PAD == 32, "one or two 16-lane rows per token");
+  constexpr int G = 64 / E_PAD;   // tokens per wave and pass
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = lane % E_PAD, sg = lane / E_PAD, seg0 = sg * E_PAD;
+  const float bv = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+  float ps = 0.0f;
+  const int extra = cand != nullptr ? min(k, E - k) : 0;
+  const int rounds = k + max(extra, gap != nullptr ? 1 : 0);
+  for (int tb = 0; tb < BT; tb += 4 * G) {
+    const int tt = tb + w * G + sg;
+    const int t = t0 + tt;
+    const bool tok = tt < BT && t < T;   // segments past the batch compute, never write
+    const float x = (tok && e < E) ? lg[(size_t)tt * E_PAD + e] : -INFINITY;
+    const float m = seg_reduce<E_PAD>(x, [](float a, float b) { return fmaxf(a, b); });
+    float pe = (tok && e < E) ? expf(x - m) : 0.0f;
+    const float sum = seg_reduce<E_PAD>(pe, [](float a, float b) { return a + b; });
+    pe = tok ? pe * (1.0f / sum) : 0.0f;   // p
+    ps += pe;
+    if (probs != nullptr && tok && e < E) probs[(size_t)t * E + e] = pe;
+    const float sc = (e < E) ? pe + bv : -INFINITY;   // selection score, fp32
+    bool taken = false;
+    int my_idx = 0, my_cand = -1;
+    float my_p = 0.0f, s_k = 0.0f, tot = 0.0f;
+    for (int r = 0; r < rounds; ++r) {
+      float bvv = (!taken && e < E) ? sc : -INFINITY;
+      int be = (!taken && e < E) ? e : 0x7fffffff;
+      float bp = pe;
+      seg_argmax<E_PAD>(bvv, be, bp);
+      const bool ok = be < E;
+      if (r >= k) {
+        if (r == k && gap != nullptr && tok && lane == seg0) gap[t] = s_k - bvv;
+        if (r - k < extra) {
+          if (ok && e == be) taken = true;
+          if (lane == seg0 + r - k) my_cand = ok ? be : -1;
+        }
+        continue;
+      }
+      s_k = bvv;
+      if (ok && e == be) taken = true;
+      tot += bp;   // sum of the chosen p in slot order
+      if (lane == seg0 + r) {
+        my_idx = be;
+        my_p = bp;
+      }
+      if (tok && lane == seg0 && ok) atomicAdd(&cnt[be], 1);
+    }
+    if (tok && e < k) {
+      topk_idx[(size_t)t * k + e] = my_idx;
+      topk_w[(size_t)t * k + e] = my_p / tot;
+      if (cand != nullptr) cand[(size_t)t * k + e] = e < extra ? my_cand : -1;
+    }
+  }
+  // the segments' partial sums of p, per expert, into lanes 0 .. E_PAD - 1
+  {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps), __float_as_uint(ps),
+                                                      false, false);
+    float v = ps;
+    if constexpr (E_PAD == 16) v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                      false, false);
+    v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    psum[0] = v;
+  }
+}
+
 // Writes the block's partial sum of p and its expert histogram (fixed order).
 template <int E_PAD>
 __device__ inline void route_block_stats(const float* psum, float (*pw)[E_PAD], const int* cnt,
@@ -324,8 +453,12 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.0f;
-  route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, cand,
-                    psum, cnt);
+  if constexpr (E_PAD <= 32)
+    route_tail_packed<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs,
+                             cand, psum, cnt);
+  else
+    route_tail<E_PAD>(&lg[0][0][0], BT, t0, T, E, k, bias, topk_idx, topk_w, gap, probs, cand,
+                      psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
 }
