@@ -217,16 +217,24 @@ static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const vo
   const int E = (int)d.n_experts;
   const int64_t C = capacity_of(d);
   const int chunk = rp.BT * (int)d.top_k;   // the route blocks' histograms serve dispatch
-  MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, nullptr,
-                       next_best ? w.cand : nullptr, w.p_part, w.cnt_part, s));
-  MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k, w.counts,
-                             f, p, w.ctr, kTileCounters, s));
-  if (next_best)
-    MOE_HIP(dispatch_next_best(d, w.topk_idx, w.cand, chunk, w.cnt_part, w.counts, w, w.offsets,
-                               w.perm_src, w.slot_pos, s));
-  else
-    MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
-                           w.perm_src, w.slot_pos, s));
+  if (rp.n_blocks == 1 && !next_best && d.dtype == MOE_DTYPE_BF16) {
+    // one route block holds the whole batch: it also does the dispatch (decode sizes)
+    const RouteDispatch fd{C, w.counts, w.offsets, w.perm_src, w.slot_pos, f, p, w.ctr,
+                           kTileCounters};
+    MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, nullptr,
+                         nullptr, w.p_part, w.cnt_part, s, &fd));
+  } else {
+    MOE_HIP(launch_route(d, x, W_router, router_bias, w.topk_idx, w.topk_w, nullptr, nullptr,
+                         next_best ? w.cand : nullptr, w.p_part, w.cnt_part, s));
+    MOE_HIP(launch_expert_scan(w.cnt_part, rp.n_blocks, E, w.p_part, d.T, (int)d.top_k,
+                               w.counts, f, p, w.ctr, kTileCounters, s));
+    if (next_best)
+      MOE_HIP(dispatch_next_best(d, w.topk_idx, w.cand, chunk, w.cnt_part, w.counts, w,
+                                 w.offsets, w.perm_src, w.slot_pos, s));
+    else
+      MOE_HIP(launch_scatter(w.topk_idx, TK, E, chunk, C, w.cnt_part, w.counts, w.offsets,
+                             w.perm_src, w.slot_pos, s));
+  }
   const GemmRows rows = token_choice_rows(d);
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
   MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));

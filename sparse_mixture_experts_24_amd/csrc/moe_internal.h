@@ -83,10 +83,24 @@ constexpr int kDispatchChunk = 1024;   // assignments per histogram block in moe
 // probs (optional, [T, E]): the router probabilities.  With topk_idx NULL no top-k is
 // taken (and the block histograms stay zero).  cand (optional, [T, k]): the experts
 // ranked k+1 .. 2k by selection score, -1 past E.
+// Dispatch done by the route kernel itself when it runs as one block (bf16 layers, T at
+// most one block's tokens): counts, f, P, offsets, perm_src and slot_pos as the
+// histogram / scan / scatter kernels give them, and nzero work counters cleared.
+struct RouteDispatch {
+  int64_t C;   // capacity, < 0: none
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_src;
+  int32_t* slot_pos;
+  float* f;
+  float* p;
+  int32_t* zero;
+  int nzero;
+};
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
                         float* probs, int32_t* cand, float* p_part, int32_t* cnt_part,
-                        hipStream_t s);
+                        hipStream_t s, const RouteDispatch* fused = nullptr);
 hipError_t launch_hist(const int32_t* idx, int64_t NA, int E, int chunk, int32_t* blk_cnt,
                        hipStream_t s);
 // zero (optional): nzero <= 256 int32 that block 0 also sets to zero.

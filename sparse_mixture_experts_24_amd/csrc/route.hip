@@ -345,12 +345,63 @@ __device__ inline void route_block_stats(const float* psum, float (*pw)[E_PAD], 
   }
 }
 
+// One-block launches (fd.offsets set): the block's histogram is the whole batch's, so the
+// dispatch follows in the same kernel: counts, f and P exactly as the expert scan forms
+// them from the one block's partials, offsets of min(count, C), and each assignment's
+// stable rank within its expert counted directly over the (at most 512) assignments.
+template <int E_PAD>
+__device__ inline void route_fused_dispatch(const RouteDispatch& fd, const float (*pw)[E_PAD],
+                                            const int* cnt, int T, int E, int k,
+                                            const int32_t* __restrict__ topk_idx) {
+  __shared__ int offs[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int c = cnt[e];
+    fd.counts[e] = c;
+    if (fd.f) fd.f[e] = (float)((double)c / (double)((int64_t)T * k));
+    if (fd.p) fd.p[e] = (float)((double)(((pw[0][e] + pw[1][e]) + pw[2][e]) + pw[3][e]) / (double)T);
+  }
+  if (tid < 64) {   // offsets: exclusive scan of min(count, C), 64 experts at a time
+    int run = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      int v = e < E ? cnt[e] : 0;
+      if (fd.C >= 0 && v > fd.C) v = (int)fd.C;
+      int incl = v;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      if (e < E) offs[e] = run + incl - v;
+      run += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) offs[E] = run;
+  }
+  for (int i = tid; i < fd.nzero; i += blockDim.x) fd.zero[i] = 0;
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) fd.offsets[e] = offs[e];
+  const int n = T * k;
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int e = topk_idx[i];
+    if ((unsigned)e >= (unsigned)E) {   // no expert (non-finite scores): dropped
+      fd.slot_pos[i] = -1;
+      continue;
+    }
+    int r = 0;
+    for (int i2 = 0; i2 < i; ++i2) r += topk_idx[i2] == e ? 1 : 0;
+    const bool keep = fd.C < 0 || (int64_t)r < fd.C;
+    const int pos = offs[e] + r;
+    fd.slot_pos[i] = keep ? pos : -1;
+    if (keep) fd.perm_src[pos] = i;
+  }
+}
+
 template <int EPW, int TPW, int KS, int R>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ gap, float* __restrict__ probs, int32_t* __restrict__ cand,
-    float* __restrict__ p_part, int32_t* __restrict__ cnt_part) {
+    float* __restrict__ p_part, int32_t* __restrict__ cnt_part, RouteDispatch fd) {
   constexpr int EW = 4 / KS;
   constexpr int E_PAD = 16 * EPW * EW;
   constexpr int BT = 16 * TPW;
@@ -461,6 +512,10 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
                       psum, cnt);
   __syncthreads();
   route_block_stats<E_PAD>(psum, pw, cnt, E, p_part, cnt_part);
+  if (fd.offsets != nullptr) {
+    __syncthreads();   // the top-k indices written above are visible to the whole block
+    route_fused_dispatch<E_PAD>(fd, pw, cnt, T, E, k, topk_idx);
+  }
 }
 
 // fp32 layers: plain FMA dot products (small correctness-sized layers).
@@ -539,13 +594,14 @@ RoutePlan route_plan(const moe_desc_t& d) {
 hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* gap,
                         float* probs, int32_t* cand, float* p_part, int32_t* cnt_part,
-                        hipStream_t s) {
+                        hipStream_t s, const RouteDispatch* fused) {
   const RoutePlan rp = route_plan(d);
   if (rp.n_blocks == 0) return hipSuccess;
   const int T = (int)d.T, dm = (int)d.d_model, E = (int)d.n_experts;
   const int k = topk_idx != nullptr ? (int)d.top_k : 0;
   const dim3 grid((unsigned)rp.n_blocks), block(256);
   if (d.dtype == MOE_DTYPE_F32) {
+    if (fused != nullptr) return hipErrorInvalidValue;   // bf16 layers only
     const float* xx = (const float*)x;
     const float* ww = (const float*)W_router;
 #define MOE_ROUTE_F32(EP)                                                                     \
@@ -563,6 +619,11 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
   }
   const bf16_t* xx = (const bf16_t*)x;
   const bf16_t* ww = (const bf16_t*)W_router;
+  RouteDispatch fd{};
+  if (fused != nullptr) {
+    if (rp.n_blocks != 1 || k == 0 || (int64_t)T * k > 512) return hipErrorInvalidValue;
+    fd = *fused;
+  }
 // R: ring slots of k-chunk fragments (8 (EPW + TPW) VGPRs each, about 200 VGPRs in all),
 // at most 8, so the loads in flight (2 (EPW + TPW) per slot) stay within what vmcnt counts.
 #define MOE_ROUTE_BF16(EPW_, TPW_, KS_)                                                      \
@@ -570,7 +631,7 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
     constexpr int R_ = (EPW_ + TPW_) <= 3 ? 8 : 200 / (8 * (EPW_ + TPW_));                      \
     hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, R_>), grid, block, 0, s, xx, ww,   \
                        bias, T, dm, E, k, topk_idx, topk_w, gap, probs, cand, p_part,         \
-                       cnt_part);                                                             \
+                       cnt_part, fd);                                                         \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTE_BF16(1, 1, 4)
