@@ -624,11 +624,14 @@ hipError_t launch_route(const moe_desc_t& d, const void* x, const void* W_router
     if (rp.n_blocks != 1 || k == 0 || (int64_t)T * k > 512) return hipErrorInvalidValue;
     fd = *fused;
   }
-// R: ring slots of k-chunk fragments (8 (EPW + TPW) VGPRs each, about 200 VGPRs in all),
-// at most 8, so the loads in flight (2 (EPW + TPW) per slot) stay within what vmcnt counts.
+// R: ring slots of k-chunk fragments (8 (EPW + TPW) VGPRs each).  Eight for the one-slab
+// layouts of small batches (latency-bound: one or few blocks); fewer where many blocks
+// share a CU and registers decide how many (measured: the Switch-shaped router takes
+// 61 us with 4 slots, 66 us with 8).  The loads in flight (2 (EPW + TPW) per slot) stay
+// within what vmcnt counts.
 #define MOE_ROUTE_BF16(EPW_, TPW_, KS_)                                                      \
   if (rp.EPW == EPW_ && rp.TPW == TPW_ && rp.KS == KS_) {                                     \
-    constexpr int R_ = (EPW_ + TPW_) <= 3 ? 8 : 200 / (8 * (EPW_ + TPW_));                      \
+    constexpr int R_ = (EPW_ + TPW_) <= 2 ? 8 : (EPW_ + TPW_) <= 3 ? 4 : 2;                   \
     hipLaunchKernelGGL((route_bf16_kernel<EPW_, TPW_, KS_, R_>), grid, block, 0, s, xx, ww,   \
                        bias, T, dm, E, k, topk_idx, topk_w, gap, probs, cand, p_part,         \
                        cnt_part, fd);                                                         \
