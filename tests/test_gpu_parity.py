@@ -33,6 +33,13 @@ CASES = {
     "k_equals_E": Workload("k_equals_E", T=50, d=64, E=4, k=4, F=128),
     "tight_capacity": Workload("tight_capacity", T=90, d=64, E=6, k=2, F=64, capacity_factor=0.01),
     "one_token": Workload("one_token", T=1, d=128, E=8, k=2, F=128, n_shared=1),
+    # one route block: the dispatch runs inside the route kernel, here with drops ...
+    "decode_capacity": Workload("decode_capacity", T=12, d=128, E=8, k=2, F=128,
+                                capacity_factor=0.5, row_scales=(2.0, 1.6, 1.3, 1.1, 1.0, 0.9,
+                                                                 0.8, 0.7)),
+    # ... and with k = 16 over 40 experts (160 assignments ranked in the block)
+    "decode_k16": Workload("decode_k16", T=10, d=128, E=40, k=16, F=64, capacity_factor=1.0,
+                           bias_range=0.05),
     # large groups with ragged remainders (64/128/256-row last tiles), dynamic tile order
     "ragged_large_groups": Workload("ragged_large_groups", T=1500, d=128, E=4, k=2, F=192,
                                     n_shared=1, bias_range=0.05),
