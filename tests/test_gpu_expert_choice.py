@@ -40,6 +40,9 @@ CASES = {
     "one_token": Workload("one_token", T=1, d=128, E=8, k=2, F=192, n_shared=1,
                           capacity_factor=1.0, routing="expert"),
     "f32": gen.workload("tiny_f32").replace(capacity_factor=1.0, routing="expert"),
+    # the largest expert count: 512 select blocks, 512-way combine lists
+    "max_experts": Workload("max_experts", T=64, d=128, E=512, k=16, F=64, n_shared=1,
+                            capacity_factor=1.0, routing="expert"),
     # T > 16384: the select kernel's widest register layout (32 tokens per thread)
     "many_tokens": Workload("many_tokens", T=20000, d=64, E=4, k=1, F=64, capacity_factor=1.0,
                             routing="expert"),

@@ -41,6 +41,9 @@ CASES = {
     "shared": Workload("shared", T=300, d=128, E=16, k=2, F=192, n_shared=1, capacity_factor=1.0,
                        row_scales=tuple(np.linspace(2.0, 0.8, 16).round(4)), routing="next_best"),
     "f32": gen.workload("tiny_f32").replace(capacity_factor=1.0, routing="next_best"),
+    # E 512, k 16: 16 candidates per token, most experts near their capacity
+    "max_experts_k16": Workload("max_experts_k16", T=64, d=128, E=512, k=16, F=64,
+                                capacity_factor=0.5, bias_range=0.05, routing="next_best"),
 }
 
 

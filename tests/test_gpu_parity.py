@@ -43,6 +43,10 @@ CASES = {
     # large groups with ragged remainders (64/128/256-row last tiles), dynamic tile order
     "ragged_large_groups": Workload("ragged_large_groups", T=1500, d=128, E=4, k=2, F=192,
                                     n_shared=1, bias_range=0.05),
+    # the largest expert count and top-k the library takes (E 512, k 16), with a shared
+    # expert and a capacity
+    "max_experts_k16": Workload("max_experts_k16", T=64, d=128, E=512, k=16, F=64, n_shared=1,
+                                capacity_factor=1.5, bias_range=0.02),
     "f32_shared_capacity": Workload("f32_shared_capacity", T=130, d=64, E=12, k=3, F=128,
                                     n_shared=1, capacity_factor=1.0, dtype="f32", bias_range=0.02),
 }
