@@ -144,10 +144,11 @@ __device__ inline float silu_fast(float z) {
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 // Output tile BM x BN, BN = 256 (gate/up: 128 gate + the matching 128 up columns).
-// BM = 32*MB rows: 256 for groups of at least SMALL_GROUP_ROWS rows (the last tile of a
-// group 64, 128 or 256, to fit the remainder), 64 below that, so small experts (decode,
-// the tail of skewed or capacity-limited routing) do not pay for 256-row MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate
-// + 32 up) and all BM A rows: MB x 2 blocks of 32x32 accumulators.
+// BM = 32*MB rows: 256 for groups that are not small (small_group below; the last tile
+// of a group 64, 128, 192 or 256 rows, to fit the remainder), 64 for small ones, so small
+// experts (decode, the tail of skewed or capacity-limited routing) do not pay for 256-row
+// MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate + 32 up)
+// and all BM A rows: MB x 2 blocks of 32x32 accumulators.
 //   * B (the weights) goes straight from global memory into MFMA operand registers,
 //     three register sets deep: the set for K-step t+2 is issued at step t, so a weight
 //     load has two steps of work to arrive;
@@ -159,7 +160,13 @@ __device__ inline float silu_fast(float z) {
 //   * each K step is one scheduling region in which the fragment reads of k16 step s+1
 //     and the global loads are interleaved with the MFMAs of step s.
 constexpr int BK = 64, LDK = BK + 8;
-constexpr int BM_BIG = 256, BM_SMALL = 64, SMALL_GROUP_ROWS = 128;
+constexpr int BM_BIG = 256, BM_SMALL = 64;
+// Row counts from which a group takes the MFMA tiles instead of 64-row tiles.  gate/up: a
+// group of 65-128 rows runs faster as one 128-row tile (its weights read once) than as
+// two 64-row streaming tiles; the down GEMM's 64-row tiles, 256 columns wide, stay ahead
+// up to 80 rows.  (Measured on the Switch-shaped layer, whose groups hold 32-320 rows:
+// gate/up 1.13 -> 1.07 ms, down 0.59 -> 0.56 ms against one bound of 128 rows for both.)
+constexpr int SMALL_GROUP_ROWS_GATED = 65, SMALL_GROUP_ROWS_DOWN = 81;
 constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 
 // Tile shape of a group with M rows: 256-row tiles for large groups, 64-row tiles for
@@ -167,12 +174,16 @@ constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 // the same block of up); down 256, or 128 for small groups when the host finds the
 // whole launch short of tiles (decode-sized batches, where the GEMM streams weights and
 // every CU must take part).
-__device__ inline bool small_group(int M) { return M < SMALL_GROUP_ROWS; }
+template <bool GATED>
+__device__ inline bool small_group(int M) {
+  return M < (GATED ? SMALL_GROUP_ROWS_GATED : SMALL_GROUP_ROWS_DOWN);
+}
 // Rows of m-tile mt (tiles start at mt * 256 in large groups, mt * 64 in small ones):
 // large groups take 256-row tiles and put their remainder in one tile of 64, 128, 192 or
 // 256 rows, whichever is the smallest that holds it.
+template <bool GATED>
 __device__ inline int m_tile_rows(int M, int mt) {
-  if (small_group(M)) return BM_SMALL;
+  if (small_group<GATED>(M)) return BM_SMALL;
   const int r = M - mt * BM_BIG;
   return r > 192 ? BM_BIG : r > 128 ? 192 : r > 64 ? 128 : 64;
 }
@@ -827,13 +838,13 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   int64_t row_begin;
   int M;
   group_rows(a, g, row_begin, M);
-  const bool sm = small_group(M);
+  const bool sm = small_group<GATED>(M);
   const int narrow = a.narrow_small;
   const int mt_g = (M + (sm ? BM_SMALL : BM_BIG) - 1) / (sm ? BM_SMALL : BM_BIG);
   const int local = (int)(tile - tiles[g]);          // ordered (n-tile, m-tile)
   const int mt = local % mt_g;
   const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
-  const int rows = m_tile_rows(M, mt);
+  const int rows = m_tile_rows<GATED>(M, mt);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
   if (!sm && rows == BM_BIG)
     gemm_bf16_tile<BM_BIG / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
@@ -880,7 +891,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ long long next_unit;
   const int N = a.N, narrow = a.narrow_small;
   auto tile_count = [N, narrow](int M) {
-    const bool sm = small_group(M);
+    const bool sm = small_group<GATED>(M);
     const int bm = sm ? BM_SMALL : BM_BIG, bn = tile_cols<GATED>(sm, narrow);
     return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   };
@@ -1049,9 +1060,10 @@ static GemmArgs base_args(const moe_desc_t& d, const GemmRows& rows, const int32
 
 // Dynamic tile order pays off where tile costs differ (large groups with 64-, 128- or
 // 256-row remainder tiles); for decode-sized batches (all groups small, every tile alike)
-// the counter round trip per tile is pure cost.
+// the counter round trip per tile is pure cost.  Taken when the groups average at least
+// 128 rows.
 static bool dynamic_tiles(const moe_desc_t& d, const GemmRows& rows) {
-  return rows.routed >= (int64_t)SMALL_GROUP_ROWS * d.n_experts;
+  return rows.routed >= (int64_t)2 * BM_SMALL * d.n_experts;
 }
 
 // Share of the CU slots of the last round left idle by n equal tiles on cus CUs.
