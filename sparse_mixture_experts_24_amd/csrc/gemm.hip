@@ -825,10 +825,20 @@ __device__ inline int k_rotation(int g, int ncol0, int nk) {
   return (int)((cb + 13u * (unsigned)g) % (unsigned)nk);
 }
 
-// One work unit: (K half, tile) of the table built in LDS.
+// One work unit: (K half, tile) of the table built in LDS.  Units from split0 on are the
+// launch's last tiles cut in two column halves (down GEMM only, see gemm_bf16_kernel):
+// unit split0 + 2 v + h is column half h of tile unit split0 + v.  Only 256- and 192-row
+// tiles are cut; of another tile, half 0 is the whole tile and half 1 is empty.
 template <bool GATED, bool FP8>
 __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
-                                               const int* tiles, int64_t ntile, int64_t unit) {
+                                               const int* tiles, int64_t ntile, int64_t unit,
+                                               int64_t split0) {
+  int half = -1;   // -1: the whole tile; 0 or 1: that column half
+  if (unit >= split0) {
+    const int64_t v = unit - split0;
+    unit = split0 + v / 2;
+    half = (int)(v & 1);
+  }
   const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
   const int ks = (int)(unit / ntile);
   const int64_t tile = unit - ks * ntile;
@@ -846,6 +856,25 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
   const int rows = m_tile_rows<GATED>(M, mt);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
+  if constexpr (!GATED) {
+    if (half >= 0) {
+      // A column half has the whole tile's K walk (rot depends on the 256-column block
+      // only), so every output element sums in the same order as in the whole tile.
+      const int nc = ncol0 + 128 * half;
+      if (nc >= a.N) return;   // a tile that holds no second half (N % 256 <= 128)
+      if (!sm && rows == BM_BIG) {
+        gemm_bf16_tile<BM_BIG / 32, 1, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, nc, k0,
+                                                   nk, rot, outp);
+        return;
+      }
+      if (!sm && rows == 192) {
+        gemm_bf16_tile<192 / 32, 1, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, nc, k0,
+                                                nk, rot, outp);
+        return;
+      }
+      if (half == 1) return;
+    }
+  }
   if (!sm && rows == BM_BIG)
     gemm_bf16_tile<BM_BIG / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
                                           rot, outp);
@@ -880,6 +909,9 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
 // Persistent kernel over the work units in table order (group, n-tile, m-tile), dealt to
 // the 8 XCDs (blocks are dispatched to XCDs round-robin) in windows of 32 consecutive
 // units, so that the m-tiles sharing a weight tile run at the same time on one L2.
+// Down GEMM with the dynamic order: when the units leave a last round at most half full
+// (r = units mod grid, 0 < 2 r <= grid), the last r units are cut into 2 r column halves,
+// so that the last round has work for more blocks and ends about half a unit earlier.
 // Without counters block b takes unit 32 (8 r + b % 8) + b / 8 of round r (grid of 256).
 // With counters (a.ctr, 8 ints, zero at launch) each block takes its XCD's next unit
 // when it is free, so blocks that drew cheap tiles (a group's 64- or 128-row remainder)
@@ -897,12 +929,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
   build_tile_table(a, tile_count, tiles);   // ends with a barrier
   const int64_t ntile = tiles[a.G];
-  const int64_t total = ntile * a.ksplit;    // work units: (K half, tile)
+  const int64_t whole = ntile * a.ksplit;    // work units: (K half, tile)
+  int64_t split0 = whole;                    // first unit cut in column halves
+  if (!GATED && a.ctr != nullptr) {
+    const int64_t r = whole % gridDim.x;
+    if (r > 0 && 2 * r <= (int64_t)gridDim.x) split0 = whole - r;
+  }
+  const int64_t total = split0 + 2 * (whole - split0);
   const int x = blockIdx.x & 7;
   if (a.ctr == nullptr) {
     const int per = gridDim.x >> 3;
     for (int64_t unit = (int64_t)x * per + (blockIdx.x >> 3); unit < total; unit += gridDim.x)
-      gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit);
+      gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit, split0);
     return;
   }
   for (;;) {
@@ -924,7 +962,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int64_t unit = next_unit;
     __syncthreads();   // read by all before thread 0 writes the next one
     if (unit < 0) break;
-    gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit);
+    gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit, split0);
   }
 }
 

@@ -43,6 +43,11 @@ CASES = {
     # large groups with ragged remainders (64/128/256-row last tiles), dynamic tile order
     "ragged_large_groups": Workload("ragged_large_groups", T=1500, d=128, E=4, k=2, F=192,
                                     n_shared=1, bias_range=0.05),
+    # large groups and a down GEMM 384 columns wide: with tile counters the launch's last
+    # down tiles run as two 128-column halves (the second half of the 128-column tail tile
+    # is empty), which must sum like the whole tiles
+    "ragged_wide_down": Workload("ragged_wide_down", T=1200, d=384, E=4, k=2, F=192,
+                                 bias_range=0.05),
     # the largest expert count and top-k the library takes (E 512, k 16), with a shared
     # expert and a capacity
     "max_experts_k16": Workload("max_experts_k16", T=64, d=128, E=512, k=16, F=64, n_shared=1,
