@@ -187,8 +187,7 @@ def main():
                                      for s in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
     log("[bench] stages (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in stage_ms.items()))
-    # moe_forward may split the down projection's K range (two fp32 partials), so the
-    # staged output agrees with it to rounding, not bit for bit.
+    # the staged kernels reproduce moe_forward bit for bit (0 expected)
     dmax = (out.float() - out2.float()).abs().max().item() if out.numel() else 0.0
     ymax = out.float().abs().max().item() if out.numel() else 0.0
     log(f"[bench] staged output vs moe_forward: max|diff| {dmax:.3e} (max|y| {ymax:.3e})")

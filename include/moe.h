@@ -86,11 +86,9 @@ const char* moe_status_str(moe_status_t status);
 moe_status_t moe_validate(const moe_desc_t* desc);
 
 /* Bytes of workspace that moe_forward and each stage entry point take for `desc` (0 if
- * desc is invalid).  Makes no HIP call.  The workspace must be 256-byte aligned.
- * A workspace sized for a larger T (all other fields equal) also serves a smaller T:
- * below the returned size but above a minimum that grows with T, moe_forward still runs
- * and only forgoes splitting the K range of its down projection over two partial
- * outputs (a layout choice for under-filled launches; results agree to rounding). */
+ * desc is invalid).  Makes no HIP call.  The workspace must be 256-byte aligned.  The
+ * size grows with T, so a workspace sized for a larger T (all other fields equal) also
+ * serves a smaller T. */
 size_t moe_workspace_bytes(const moe_desc_t* desc);
 
 /* Capacity C for `desc`: max(floor(cf * k * T / E), k), or -1 when cf <= 0 (no limit)

@@ -23,13 +23,11 @@ __device__ inline void store4<bf16_t>(bf16_t* out, int64_t i, float4 v) {
   *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
 }
 
-// Yp2 (optional): second partial of a K-split down GEMM; a slot's output is Yp + Yp2.
 // The slots are read KB at a time, all loads of a batch issued before any is used (a
-// dropped slot loads row 0 and contributes nothing), so each thread keeps KB (or 2 KB)
-// 16-byte loads in flight; the sum runs over the slots in ascending order.
-template <typename OutT, int KB, bool SPLIT>
+// dropped slot loads row 0 and contributes nothing), so each thread keeps KB 16-byte loads
+// in flight; the sum runs over the slots in ascending order.
+template <typename OutT, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp,
-                                                      const float* __restrict__ Yp2,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ w, int T, int k,
                                                       int d, int shared, OutT* __restrict__ out) {
@@ -54,13 +52,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         ok[q] = pos >= 0;
         const int64_t off = (int64_t)(ok[q] ? pos : 0) * d + c;
         v[q] = *reinterpret_cast<const float4*>(Yp + off);
-        if constexpr (SPLIT) {
-          const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + off);
-          v[q].x += v2.x;
-          v[q].y += v2.y;
-          v[q].z += v2.z;
-          v[q].w += v2.w;
-        }
       }
 #pragma unroll
       for (int q = 0; q < KB; ++q) {
@@ -73,14 +64,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
     if (shared) {
-      float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
-      if constexpr (SPLIT) {
-        const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + srow * d + c);
-        v.x += v2.x;
-        v.y += v2.y;
-        v.z += v2.z;
-        v.w += v2.w;
-      }
+      const float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -90,40 +74,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-template <typename OutT, bool SPLIT>
-static void launch_combine_t(const moe_desc_t& d, const float* Yp, const float* Yp2,
-                             const int32_t* slot_pos, const float* topk_w, OutT* out,
-                             hipStream_t s) {
+template <typename OutT>
+static void launch_combine_o(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
+                             const float* topk_w, OutT* out, hipStream_t s) {
   const dim3 grid((unsigned)d.T), block(256);
   const int T = (int)d.T, k = (int)d.top_k, dm = (int)d.d_model, sh = (int)d.n_shared;
   if (k == 1)
-    hipLaunchKernelGGL((combine_kernel<OutT, 1, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
-                       topk_w, T, k, dm, sh, out);
+    hipLaunchKernelGGL((combine_kernel<OutT, 1>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
+                       dm, sh, out);
   else if (k == 2)
-    hipLaunchKernelGGL((combine_kernel<OutT, 2, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
-                       topk_w, T, k, dm, sh, out);
+    hipLaunchKernelGGL((combine_kernel<OutT, 2>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
+                       dm, sh, out);
   else
-    hipLaunchKernelGGL((combine_kernel<OutT, 4, SPLIT>), grid, block, 0, s, Yp, Yp2, slot_pos,
-                       topk_w, T, k, dm, sh, out);
+    hipLaunchKernelGGL((combine_kernel<OutT, 4>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
+                       dm, sh, out);
 }
 
-template <typename OutT>
-static void launch_combine_o(const moe_desc_t& d, const float* Yp, const float* Yp2,
-                             const int32_t* slot_pos, const float* topk_w, OutT* out,
-                             hipStream_t s) {
-  if (Yp2)
-    launch_combine_t<OutT, true>(d, Yp, Yp2, slot_pos, topk_w, out, s);
-  else
-    launch_combine_t<OutT, false>(d, Yp, Yp2, slot_pos, topk_w, out, s);
-}
-
-hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
-                          const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s) {
+hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
+                          const float* topk_w, void* out, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   if (d.out_dtype == MOE_DTYPE_F32)
-    launch_combine_o<float>(d, Yp, Yp2, slot_pos, topk_w, (float*)out, s);
+    launch_combine_o<float>(d, Yp, slot_pos, topk_w, (float*)out, s);
   else
-    launch_combine_o<bf16_t>(d, Yp, Yp2, slot_pos, topk_w, (bf16_t*)out, s);
+    launch_combine_o<bf16_t>(d, Yp, slot_pos, topk_w, (bf16_t*)out, s);
   return hipGetLastError();
 }
 

@@ -181,9 +181,8 @@ __device__ inline void ec_store4<bf16_t>(bf16_t* out, int64_t i, float4 v) {
 // One block per token.  Wave 0 lists the token's taken experts in ascending order (row and
 // weight, through LDS); then each thread sums float4 columns over the list, four rows in
 // flight at a time.
-template <typename OutT, bool SPLIT>
+template <typename OutT>
 __global__ __launch_bounds__(256) void ec_combine_kernel(const float* __restrict__ Yp,
-                                                         const float* __restrict__ Yp2,
                                                          const int32_t* __restrict__ slot,
                                                          const float* __restrict__ probs, int E,
                                                          int d, int shared, int64_t shared_row0,
@@ -220,13 +219,6 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const float* __restrict
         const int j = j0 + q;
         const int64_t off = (int64_t)(j < n ? rows[j] : rows[j0]) * d + c;
         v[q] = *reinterpret_cast<const float4*>(Yp + off);
-        if constexpr (SPLIT) {
-          const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + off);
-          v[q].x += v2.x;
-          v[q].y += v2.y;
-          v[q].z += v2.z;
-          v[q].w += v2.w;
-        }
       }
 #pragma unroll
       for (int q = 0; q < KB; ++q) {
@@ -239,14 +231,7 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const float* __restrict
       }
     }
     if (shared) {
-      float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
-      if constexpr (SPLIT) {
-        const float4 v2 = *reinterpret_cast<const float4*>(Yp2 + srow * d + c);
-        v.x += v2.x;
-        v.y += v2.y;
-        v.z += v2.z;
-        v.w += v2.w;
-      }
+      const float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -256,28 +241,17 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const float* __restrict
   }
 }
 
-template <typename OutT>
-static void ec_combine_o(const moe_desc_t& d, int64_t shared_row0, const float* Yp,
-                         const float* Yp2, const int32_t* slot, const float* probs, OutT* out,
-                         hipStream_t s) {
+hipError_t launch_ec_combine(const moe_desc_t& d, int64_t shared_row0, const float* Yp,
+                             const int32_t* slot, const float* probs, void* out, hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
   const dim3 grid((unsigned)d.T), block(256);
   const int E = (int)d.n_experts, dm = (int)d.d_model, sh = (int)d.n_shared;
-  if (Yp2)
-    hipLaunchKernelGGL((ec_combine_kernel<OutT, true>), grid, block, 0, s, Yp, Yp2, slot, probs,
-                       E, dm, sh, shared_row0, out);
-  else
-    hipLaunchKernelGGL((ec_combine_kernel<OutT, false>), grid, block, 0, s, Yp, Yp2, slot,
-                       probs, E, dm, sh, shared_row0, out);
-}
-
-hipError_t launch_ec_combine(const moe_desc_t& d, int64_t shared_row0, const float* Yp,
-                             const float* Yp2, const int32_t* slot, const float* probs,
-                             void* out, hipStream_t s) {
-  if (d.T == 0) return hipSuccess;
   if (d.out_dtype == MOE_DTYPE_F32)
-    ec_combine_o<float>(d, shared_row0, Yp, Yp2, slot, probs, (float*)out, s);
+    hipLaunchKernelGGL(ec_combine_kernel<float>, grid, block, 0, s, Yp, slot, probs, E, dm, sh,
+                       shared_row0, (float*)out);
   else
-    ec_combine_o<bf16_t>(d, shared_row0, Yp, Yp2, slot, probs, (bf16_t*)out, s);
+    hipLaunchKernelGGL(ec_combine_kernel<bf16_t>, grid, block, 0, s, Yp, slot, probs, E, dm, sh,
+                       shared_row0, (bf16_t*)out);
   return hipGetLastError();
 }
 

@@ -45,8 +45,6 @@ struct GemmArgs {
   int64_t shared_row0;    // T*k: first row of the shared expert
   int T, topk, E, G, N, K, n_tiles;
   int narrow_small;       // small groups take half-width tiles (gate/up 64, down 128 columns)
-  int ksplit;             // 1, or 2: the K range in two halves, partial sums to out / out2
-  void* out2;             // second partial output (ksplit == 2)
   int* ctr;               // NULL, or 8 per-XCD unit counters, zero at launch
   const float* sc0;       // 8-bit weights: per-row scales of B0 [G, N] (else unused)
   const float* sc1;       // 8-bit weights: per-row scales of B1 (gated)
@@ -593,7 +591,7 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
   }
 }
 
-// One output tile over K steps [k0, k0 + nk) (the whole K unless split), into outp.
+// One output tile over K steps [k0, k0 + nk) (callers pass the whole K), into outp.
 template <int MB, int NB, bool GATED, bool FP8>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
                                                int64_t row_begin, int M, int m0, int ncol0,
@@ -825,7 +823,7 @@ __device__ inline int k_rotation(int g, int ncol0, int nk) {
   return (int)((cb + 13u * (unsigned)g) % (unsigned)nk);
 }
 
-// One work unit: (K half, tile) of the table built in LDS.  Units from split0 on are the
+// One work unit: a tile of the table built in LDS.  Units from split0 on are the
 // launch's last tiles cut in two column halves (down GEMM only, see gemm_bf16_kernel):
 // unit split0 + 2 v + h is column half h of tile unit split0 + v.  Only 256- and 192-row
 // tiles are cut; of another tile, half 0 is the whole tile and half 1 is empty.
@@ -839,11 +837,9 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
     unit = split0 + v / 2;
     half = (int)(v & 1);
   }
-  const int nk_all = a.K / BK, nk_half = (nk_all + a.ksplit - 1) / a.ksplit;
-  const int ks = (int)(unit / ntile);
-  const int64_t tile = unit - ks * ntile;
-  const int k0 = ks * nk_half, nk = min(nk_half, nk_all - k0);
-  void* outp = ks == 0 ? a.out : a.out2;
+  const int64_t tile = unit;
+  const int k0 = 0, nk = a.K / BK;
+  void* outp = a.out;
   const int g = find_group(tiles, a.G, tile);
   int64_t row_begin;
   int M;
@@ -929,7 +925,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
   build_tile_table(a, tile_count, tiles);   // ends with a barrier
   const int64_t ntile = tiles[a.G];
-  const int64_t whole = ntile * a.ksplit;    // work units: (K half, tile)
+  const int64_t whole = ntile;               // work units: the tiles
   int64_t split0 = whole;                    // first unit cut in column halves
   if (!GATED && a.ctr != nullptr) {
     const int64_t r = whole % gridDim.x;
@@ -1131,7 +1127,6 @@ hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void*
   a.N = (int)d.d_ff;
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
-  a.ksplit = 1;
   a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
   {
     // Every group fits a skinny tile (at most T rows each): take 64-column tiles when that
@@ -1148,24 +1143,8 @@ hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void*
   return ew.fp8 ? run_bf16<true, true>(a, mt, s) : run_bf16<true, false>(a, mt, s);
 }
 
-// Whether moe_forward splits the down GEMM's K range in two: when the estimated number
-// of 256 x 256 output tiles leaves the last round of a 256-CU chip at most 3/4 full and
-// doubling the work units saves at least a quarter of a round.  Host-only arithmetic
-// (no device query), so the workspace size depends on the description alone.
-bool down_split_k(const moe_desc_t& d, const GemmRows& rows) {
-  if (d.dtype != MOE_DTYPE_BF16 || d.d_ff / BK < 2) return false;
-  const int64_t TK = rows.routed;
-  if (TK == 0) return false;
-  const int64_t m_tiles = ceil_div(TK, BM_BIG) + std::min<int64_t>(d.n_experts, TK) +
-                          (d.n_shared ? ceil_div(d.T, BM_BIG) : 0);
-  const int64_t est = m_tiles * ceil_div(d.d_model, 256), cus = 256;
-  if (est > 8 * cus) return false;
-  const double r1 = (double)ceil_div(est, cus), r2 = 0.5 * (double)ceil_div(2 * est, cus);
-  return r2 <= r1 - 0.25;
-}
-
 hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
-                       const int32_t* offsets, const ExpertWeights& ew, float* Yp, float* Yp2,
+                       const int32_t* offsets, const ExpertWeights& ew, float* Yp,
                        int32_t* ctr, hipStream_t s) {
   const bool bf = d.dtype == MOE_DTYPE_BF16;
   GemmArgs a = base_args(d, rows, offsets);
@@ -1182,8 +1161,6 @@ hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
     const int64_t groups = std::min<int64_t>(d.n_experts + d.n_shared, rows.routed + d.n_shared);
     a.narrow_small = groups * ceil_div(d.d_model, 256) < 2 * (int64_t)device_cu_count();
   }
-  a.ksplit = (bf && Yp2) ? 2 : 1;
-  a.out2 = Yp2;
   a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
   const int64_t mt = max_m_tiles(d, rows, BM_SMALL) * ceil_div(d.d_model, 128);
   if (!bf) return run_f32<false>(a, max_m_tiles(d, rows, 64), s);

@@ -60,19 +60,13 @@ Workspace carve_workspace(const moe_desc_t& d, void* base) {
   w.ocounts = (int32_t*)take(E * 4);
   w.H = take((size_t)rows * d.d_ff * esz);
   w.Yp = (float*)take((size_t)rows * d.d_model * 4);
-  w.bytes = off;   // the minimum; monotone in T
-  // Optional tail: the second partial of a split down GEMM, used when the workspace has
-  // room for it (moe_workspace_bytes asks for it).
-  w.Yp2 = down_split_k(d, token_choice_rows(d)) ? (float*)take((size_t)rows * d.d_model * 4)
-                                                : nullptr;
-  w.bytes_full = off;
+  w.bytes = off;   // monotone in T
   return w;
 }
 
 static moe_status_t check_ws(const moe_desc_t& d, void* ws, size_t bytes, Workspace& w) {
   w = carve_workspace(d, ws);
   if (!ws || bytes < w.bytes || ((uintptr_t)ws & 255u)) return MOE_E_WORKSPACE;
-  if (bytes < w.bytes_full) w.Yp2 = nullptr;
   return MOE_OK;
 }
 
@@ -127,7 +121,7 @@ static moe_status_t experts_impl(const moe_desc_t* desc, const void* x, const in
   void* h = H ? H : w.H;
   MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
   MOE_HIP(launch_gate_up(d, token_choice_rows(d), x, perm_src, offsets, ew, h, w.ctr, s));
-  MOE_HIP(launch_down(d, token_choice_rows(d), h, offsets, ew, Yp, nullptr, w.ctr + 8, s));
+  MOE_HIP(launch_down(d, token_choice_rows(d), h, offsets, ew, Yp, w.ctr + 8, s));
   return MOE_OK;
 }
 
@@ -171,7 +165,7 @@ static moe_status_t down_impl(const moe_desc_t* desc, const void* H, const int32
   if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
-  MOE_HIP(launch_down(*desc, token_choice_rows(*desc), H, offsets, ew, Yp, nullptr,
+  MOE_HIP(launch_down(*desc, token_choice_rows(*desc), H, offsets, ew, Yp,
                       ctr ? ctr + 8 : nullptr, s));
   return MOE_OK;
 }
@@ -237,8 +231,8 @@ static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const vo
   }
   const GemmRows rows = token_choice_rows(d);
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
-  MOE_HIP(launch_combine(d, w.Yp, w.Yp2, w.slot_pos, w.topk_w, out, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + 8, s));
+  MOE_HIP(launch_combine(d, w.Yp, w.slot_pos, w.topk_w, out, s));
   return MOE_OK;
 }
 
@@ -292,15 +286,12 @@ WorkspaceEC carve_workspace_ec(const moe_desc_t& d, void* base) {
   w.H = take((size_t)rows * d.d_ff * esz);
   w.Yp = (float*)take((size_t)rows * d.d_model * 4);
   w.bytes = off;
-  w.Yp2 = down_split_k(d, gr) ? (float*)take((size_t)rows * d.d_model * 4) : nullptr;
-  w.bytes_full = off;
   return w;
 }
 
 static moe_status_t check_ws_ec(const moe_desc_t& d, void* ws, size_t bytes, WorkspaceEC& w) {
   w = carve_workspace_ec(d, ws);
   if (!ws || bytes < w.bytes || ((uintptr_t)ws & 255u)) return MOE_E_WORKSPACE;
-  if (bytes < w.bytes_full) w.Yp2 = nullptr;
   return MOE_OK;
 }
 
@@ -326,7 +317,7 @@ moe_status_t moe_validate(const moe_desc_t* desc) { return validate(desc); }
 
 size_t moe_workspace_bytes(const moe_desc_t* desc) {
   if (validate(desc) != MOE_OK) return 0;
-  return carve_workspace(*desc, nullptr).bytes_full;
+  return carve_workspace(*desc, nullptr).bytes;
 }
 
 int64_t moe_capacity(const moe_desc_t* desc) {
@@ -407,7 +398,7 @@ moe_status_t moe_combine(const moe_desc_t* desc, const float* Yp, const int32_t*
   const moe_desc_t& d = *desc;
   if (d.T > 0 && (!Yp || !slot_pos || !topk_w || !out)) return MOE_E_NULL;
   if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_combine(d, Yp, nullptr, slot_pos, topk_w, out, (hipStream_t)stream));
+  MOE_HIP(launch_combine(d, Yp, slot_pos, topk_w, out, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -463,7 +454,7 @@ extern "C" {
 
 size_t moe_workspace_bytes_expert_choice(const moe_desc_t* desc) {
   if (validate_ec(desc) != MOE_OK) return 0;
-  return carve_workspace_ec(*desc, nullptr).bytes_full;
+  return carve_workspace_ec(*desc, nullptr).bytes;
 }
 
 int64_t moe_capacity_expert_choice(const moe_desc_t* desc) {
@@ -511,7 +502,7 @@ moe_status_t moe_combine_expert_choice(const moe_desc_t* desc, const float* Yp,
   const moe_desc_t& d = *desc;
   if (d.T > 0 && (!Yp || !slot || !probs || !out)) return MOE_E_NULL;
   if (!aligned16(Yp) || !aligned16(out)) return MOE_E_UNSUPPORTED;
-  MOE_HIP(launch_ec_combine(d, expert_choice_rows(d).routed, Yp, nullptr, slot, probs, out,
+  MOE_HIP(launch_ec_combine(d, expert_choice_rows(d).routed, Yp, slot, probs, out,
                             (hipStream_t)stream));
   return MOE_OK;
 }
@@ -549,8 +540,8 @@ moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
   MOE_HIP(launch_ec_select(w.probs, (int)d.T, E, (int)expert_choice_capacity(d), w.perm_src,
                            w.offsets, w.slot, f, s));
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.Yp2, w.ctr + 8, s));
-  MOE_HIP(launch_ec_combine(d, rows.routed, w.Yp, w.Yp2, w.slot, w.probs, out, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + 8, s));
+  MOE_HIP(launch_ec_combine(d, rows.routed, w.Yp, w.slot, w.probs, out, s));
   return MOE_OK;
 }
 

@@ -51,9 +51,7 @@ struct Workspace {
   int32_t* cand;       // [T*k] next-best candidates (overflow redirect)
   int32_t* offer;      // [T*k] expert offered each dropped assignment, or -1
   int32_t* ocounts;    // [E] offers per expert
-  float* Yp2;          // second partial of the split down GEMM, or NULL
-  size_t bytes;        // minimum size (without Yp2)
-  size_t bytes_full;   // with Yp2 when the layer splits its down GEMM
+  size_t bytes;        // total size
 };
 Workspace carve_workspace(const moe_desc_t& d, void* base);
 
@@ -69,8 +67,7 @@ struct WorkspaceEC {
   void* H;             // [E*C + S*T, F] dtype
   float* Yp;           // [E*C + S*T, d]
   int32_t* ctr;        // kTileCounters
-  float* Yp2;          // or NULL
-  size_t bytes, bytes_full;
+  size_t bytes;        // total size
 };
 // C of an expert-choice layer: min(T, max(floor(cf k T / E), k)); -1 when cf <= 0.
 int64_t expert_choice_capacity(const moe_desc_t& d);
@@ -145,18 +142,15 @@ inline GemmRows token_choice_rows(const moe_desc_t& d) { return {d.T * d.top_k, 
 hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void* x,
                           const int32_t* perm_src, const int32_t* offsets,
                           const ExpertWeights& ew, void* H, int32_t* ctr, hipStream_t s);
-// Yp2 non-NULL (bf16 layers): K split in two, partial sums in Yp and Yp2.
 // ctr: NULL (static tile order) or 8 int32 work counters, zero at launch.
 hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
-                       const int32_t* offsets, const ExpertWeights& ew, float* Yp, float* Yp2,
+                       const int32_t* offsets, const ExpertWeights& ew, float* Yp,
                        int32_t* ctr, hipStream_t s);
 // Sets n int32 to zero (a kernel, so that it may sit in a captured graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 constexpr int kTileCounters = 16;   // 8 per grouped GEMM
-bool down_split_k(const moe_desc_t& d, const GemmRows& rows);
-// Yp2 non-NULL: the per-slot outputs are Yp + Yp2.
-hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const float* Yp2,
-                          const int32_t* slot_pos, const float* topk_w, void* out, hipStream_t s);
+hipError_t launch_combine(const moe_desc_t& d, const float* Yp, const int32_t* slot_pos,
+                          const float* topk_w, void* out, hipStream_t s);
 
 // Expert choice: expert e takes the C tokens with the largest probs[:, e] (ties to the
 // lower token), rows [e C, (e+1) C) in ascending token order; slot [T, E] gets each
@@ -166,9 +160,8 @@ constexpr int kMaxExpertChoiceTokens = 32768;
 hipError_t launch_ec_select(const float* probs, int T, int E, int C, int32_t* perm_src,
                             int32_t* offsets, int32_t* slot, float* f, hipStream_t s);
 // out[t] = sum over e ascending with slot[t, e] >= 0 of probs[t, e] * Yp[slot[t, e]]
-// (+ Yp[shared_row0 + t] with a shared expert); Yp2 as in launch_combine.
+// (+ Yp[shared_row0 + t] with a shared expert).
 hipError_t launch_ec_combine(const moe_desc_t& d, int64_t shared_row0, const float* Yp,
-                             const float* Yp2, const int32_t* slot, const float* probs,
-                             void* out, hipStream_t s);
+                             const int32_t* slot, const float* probs, void* out, hipStream_t s);
 
 }  // namespace moe
