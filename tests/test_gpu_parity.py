@@ -193,11 +193,14 @@ def test_forward_is_deterministic(case):
         assert torch.equal(u, v)
 
 
-def test_batch_consistency():
+@pytest.mark.parametrize("name", ["fine_shared_bias", "ragged_wide_down", "prefill_skewed"])
+def test_batch_consistency(name):
     """Without a capacity, a token's output does not depend on the rest of the batch:
     batch 1 and batch 64 give bit-identical rows ("Mixture-of-experts in practice",
-    inference-stability section, batch-consistency check)."""
-    wl = CASES["fine_shared_bias"]
+    inference-stability section, batch-consistency check).  The larger cases run the
+    full batch with 256-row tiles, the dynamic tile order and the down GEMM's column
+    halves, the sub-batches with 64-row and skinny tiles."""
+    wl = CASES[name]
     inp = to_dev(gen.make_inputs(wl), DEV)
     args = (inp["router_bias"], inp["W_gate"], inp["W_up"], inp["W_down"], wl.k, 0.0)
     full, _, _ = moe.forward(inp["x"], inp["W_router"], *args)
