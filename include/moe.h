@@ -13,8 +13,9 @@
  *   statistics f_e = #assignments to e / (T k) (before any capacity drop);
  *              P_e = mean_t p[t, e]   (memo, auxiliary-loss section)
  *   dispatch   the T*k assignments, flattened row-major (i = t*k + j), are grouped by
- *              expert in stable order; with a capacity C = max(floor(cf k T / E), k) the
- *              first C of each expert are kept, the rest dropped
+ *              expert in stable order; with a capacity C = max(floor(cf k T / E), k) (the
+ *              product exact on the float32 cf; see moe_capacity) the first C of
+ *              each expert are kept, the rest dropped
  *              ("Mixture-of-experts in practice: routing, load balancing and parallel
  *              configuration", deepseekmodel.com, routing-math and expert-parallel
  *              sections)
@@ -92,8 +93,10 @@ moe_status_t moe_validate(const moe_desc_t* desc);
 size_t moe_workspace_bytes(const moe_desc_t* desc);
 
 /* Capacity C for `desc`: max(floor(cf * k * T / E), k), or -1 when cf <= 0 (no limit)
- * or desc is invalid.  ("Mixture-of-experts in practice", routing-math section.)
- * Makes no HIP call. */
+ * or desc is invalid.  ("Mixture-of-experts in practice", routing-math section.)  The
+ * product is exact on the float32 value of capacity_factor (no rounding, no evaluation
+ * order: cf = 0.7 is 0.699999988..., so k T / E = 10 gives C = 6); a C above T * k
+ * keeps every assignment and is returned as T * k.  Makes no HIP call. */
 int64_t moe_capacity(const moe_desc_t* desc);
 
 /* The whole layer: route -> dispatch -> experts -> combine.

@@ -27,8 +27,9 @@ notes of the repository):
   * ties in the selection score go to the lower expert index, and slots are ordered
     by selection score, highest first;
   * f_e counts top-k assignments before any capacity drop and is normalised by T*k;
-  * capacity C = max(floor(cf * k * T / E), k); assignments are ranked per expert in
-    row-major (token, slot) order and the first C are kept;
+  * capacity C = max(floor(cf * k * T / E), k), the product taken exactly on the
+    float32 value of cf (C above T*k reported as T*k); assignments are ranked per expert
+    in row-major (token, slot) order and the first C are kept;
   * a dropped assignment contributes zero; the layer adds no residual;
   * overflow handed to the next-best expert ([book ch.30] 30.5.2) is one redirect round:
     each assignment dropped by the capacity goes to its token's next unused expert by
@@ -53,6 +54,7 @@ closed forms, library routines and brute force.  Large-shape absolute values are
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -185,13 +187,21 @@ def balance_loss(f, P) -> float:
 def capacity(T: int, k: int, E: int, cf: float):
     """Per-expert capacity C = max(floor(cf * k * T / E), k); None when cf <= 0.
 
-    [MoE practice] routing-math section (capacity from the expected load, at least k);
-    [book ch.30] 30.5.2 and [MoE guide] expert-capacity section give (T/E)*cf, the same
-    number for top-1.
+    [MoE practice] routing-math section (capacity from the expected load k*T/E times the
+    capacity factor, truncated, at least k); [book ch.30] 30.5.2 and [MoE guide]
+    expert-capacity section give (T/E)*cf, the same number for top-1.
+
+    The pages write the product in three orders, which round differently in binary
+    floating point.  Reading taken: cf is the float32 value the layer's descriptor
+    carries, and the product is exact (rational arithmetic, floored once), so no
+    evaluation order enters.  A C above T*k keeps every assignment (an expert holds at
+    most one slot of each token), so such a C is reported as T*k.
     """
-    if cf is None or cf <= 0:
+    if cf is None or not cf > 0:
         return None
-    return max(int(math.floor(cf * k * T / E)), k)
+    cf32 = Fraction(float(np.float32(cf)))          # the exact binary value carried
+    raw = math.floor(cf32 * k * T / E)
+    return max(min(raw, T * k), k)
 
 
 def dispatch(idx: np.ndarray, E: int, C=None):

@@ -3,6 +3,8 @@
 // include/moe.h.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -70,13 +72,33 @@ static moe_status_t check_ws(const moe_desc_t& d, void* ws, size_t bytes, Worksp
   return MOE_OK;
 }
 
+// Per-expert capacity C = max(floor(cf k T / E), k) ("Mixture-of-experts in practice",
+// routing-math section: the expected load k T / E times the capacity factor, truncated,
+// at least k), -1 without a capacity (cf <= 0).  The product is exact on the float32 cf
+// of the descriptor: cf = m 2^s with an integer m < 2^24, so floor(m k T 2^s / E) is
+// integer arithmetic (m k T < 2^54 under validate()'s bounds) and no evaluation order or
+// rounding enters.  A C above T k keeps every assignment (an expert holds at most one
+// slot per token), so it is reported as T k, which also keeps C within 32 bits.
 static int64_t capacity_of(const moe_desc_t& d) {
   if (!(d.capacity_factor > 0.0f)) return -1;
-  const double c = floor((double)d.capacity_factor * (double)d.top_k * (double)d.T /
-                         (double)d.n_experts);
-  int64_t C = (int64_t)c;
-  if (C < d.top_k) C = d.top_k;
-  return C;
+  const int64_t all = d.T * d.top_k;
+  int e2 = 0;
+  const float fr = frexpf(d.capacity_factor, &e2);        // cf = fr 2^e2, fr in [0.5, 1)
+  const uint64_t m = (uint64_t)ldexpf(fr, 24);             // exact: 24 significant bits
+  const int s = e2 - 24;                                   // cf = m 2^s
+  const unsigned __int128 num = (unsigned __int128)m * (uint64_t)d.top_k * (uint64_t)d.T;
+  const uint64_t E = (uint64_t)d.n_experts;
+  int64_t raw;
+  if (num == 0) {
+    raw = 0;
+  } else if (s >= 0) {
+    // num >= 1 and E <= 2^10, so a shift of 50 or more gives at least 2^40 > T k
+    raw = s >= 50 ? all : (int64_t)std::min<unsigned __int128>((num << s) / E, all);
+  } else {
+    const unsigned __int128 q = num / E;
+    raw = -s >= 64 ? 0 : (int64_t)std::min<unsigned __int128>(q >> -s, all);
+  }
+  return raw < d.top_k ? d.top_k : raw;
 }
 
 #define MOE_HIP(call)                       \

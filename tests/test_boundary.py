@@ -83,13 +83,30 @@ def test_status_strings(L):
         assert L.moe_status_str(code).decode().startswith(moe.STATUS[code])
 
 
-def test_capacity_matches_the_closed_form(L):
-    for T, E, k, cf in [(16384, 64, 1, 1.25), (10, 4, 1, 1.25), (3, 64, 2, 1.0), (4096, 8, 2, 1.1),
-                        (100, 8, 2, 0.0), (100, 8, 2, -1.0)]:
+def test_capacity_matches_the_oracle(L):
+    """moe_capacity against the oracle's capacity (exact product on the float32 cf, C above
+    T k reported as T k): the golden cases at integer boundaries, huge and tiny factors,
+    and a dense sweep of decimal factors over token, top-k and expert counts."""
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "capacity_examples.json")))
+    cases = [(c["T"], c["E"], c["k"], c["cf"]) for c in gold["cases"]]
+    cases += [(100, 8, 2, 0.0), (100, 8, 2, -1.0), (40, 8, 2, 3.0e38), (0, 8, 2, 1e30)]
+    for T, E, k, cf in cases:
         d = desc(T=T, n_experts=E, top_k=k, capacity_factor=cf)
-        c = L.moe_capacity(ctypes.byref(d))
         ref = oracle.capacity(T, k, E, cf)
-        assert c == (-1 if ref is None else ref)
+        assert L.moe_capacity(ctypes.byref(d)) == (-1 if ref is None else ref), (T, E, k, cf)
+    for c in gold["cases"]:
+        d = desc(T=c["T"], n_experts=c["E"], top_k=c["k"], capacity_factor=c["cf"])
+        assert L.moe_capacity(ctypes.byref(d)) == c["C"], c
+    n = 0
+    for k, T, E in [(1, 16384, 64), (2, 4096, 8), (2, 250, 3), (2, 40, 8), (8, 8192, 256),
+                    (3, 77, 7), (1, 1, 1), (16, 5, 512), (4, 1000, 100), (1, 123, 9)]:
+        for i in range(1, 401):
+            cf = i / 100.0
+            d = desc(T=T, n_experts=E, top_k=k, capacity_factor=cf)
+            assert L.moe_capacity(ctypes.byref(d)) == oracle.capacity(T, k, E, cf), (T, E, k, cf)
+            n += 1
+    assert n == 4000
 
 
 def test_workspace_grows_with_tokens(L):
@@ -154,7 +171,8 @@ def test_expert_choice_validation_and_capacity(L):
     """Expert choice needs a capacity factor > 0 and T within the select kernel's reach;
     its C is the token-choice capacity capped at T."""
     for T, E, k, cf in [(4096, 8, 2, 1.0), (10, 8, 2, 1.0), (10, 8, 2, 50.0), (1, 4, 1, 0.5),
-                        (16384, 64, 1, 1.25)]:
+                        (16384, 64, 1, 1.25), (40, 8, 2, 0.7), (250, 3, 2, 0.03), (40, 8, 2, 1e20),
+                        (3, 64, 2, 1e30)]:
         d = desc(T=T, n_experts=E, top_k=k, capacity_factor=cf)
         assert L.moe_capacity_expert_choice(ctypes.byref(d)) == oracle.expert_choice_capacity(
             T, k, E, cf)

@@ -40,6 +40,9 @@ CASES = {
     "one_token": Workload("one_token", T=1, d=128, E=8, k=2, F=192, n_shared=1,
                           capacity_factor=1.0, routing="expert"),
     "f32": gen.workload("tiny_f32").replace(capacity_factor=1.0, routing="expert"),
+    # float32 cf just below 0.7: C = 6 at k T / E = 10
+    "capacity_boundary": Workload("capacity_boundary", T=40, d=64, E=8, k=2, F=64,
+                                  capacity_factor=0.7, routing="expert"),
     # the largest expert count: 512 select blocks, 512-way combine lists
     "max_experts": Workload("max_experts", T=64, d=128, E=512, k=16, F=64, n_shared=1,
                             capacity_factor=1.0, routing="expert"),

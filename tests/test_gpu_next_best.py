@@ -41,6 +41,11 @@ CASES = {
     "shared": Workload("shared", T=300, d=128, E=16, k=2, F=192, n_shared=1, capacity_factor=1.0,
                        row_scales=tuple(np.linspace(2.0, 0.8, 16).round(4)), routing="next_best"),
     "f32": gen.workload("tiny_f32").replace(capacity_factor=1.0, routing="next_best"),
+    # float32 cf just below 0.7: C = 69 at k T / E = 100
+    "capacity_boundary": Workload("capacity_boundary", T=400, d=64, E=8, k=2, F=64,
+                                  capacity_factor=0.7,
+                                  row_scales=tuple(np.linspace(2.0, 0.8, 8).round(4)),
+                                  routing="next_best"),
     # E 512, k 16: 16 candidates per token, most experts near their capacity
     "max_experts_k16": Workload("max_experts_k16", T=64, d=128, E=512, k=16, F=64,
                                 capacity_factor=0.5, bias_range=0.05, routing="next_best"),

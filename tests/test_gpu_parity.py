@@ -52,6 +52,16 @@ CASES = {
     # expert and a capacity
     "max_experts_k16": Workload("max_experts_k16", T=64, d=128, E=512, k=16, F=64, n_shared=1,
                                 capacity_factor=1.5, bias_range=0.02),
+    # capacity factors whose float32 value sits just below (0.7) or above (0.3) a decimal
+    # that makes cf k T / E an integer: C = 6 (one route block, fused dispatch) and 69
+    "capacity_boundary_fused": Workload("capacity_boundary_fused", T=40, d=64, E=8, k=2, F=64,
+                                        capacity_factor=0.7,
+                                        row_scales=tuple(np.linspace(2.0, 0.8, 8).round(4))),
+    "capacity_boundary": Workload("capacity_boundary", T=400, d=64, E=8, k=2, F=64,
+                                  capacity_factor=0.7,
+                                  row_scales=tuple(np.linspace(2.0, 0.8, 8).round(4))),
+    "capacity_above_decimal": Workload("capacity_above_decimal", T=400, d=64, E=8, k=2, F=64,
+                                       capacity_factor=0.3),
     "f32_shared_capacity": Workload("f32_shared_capacity", T=130, d=64, E=12, k=3, F=128,
                                     n_shared=1, capacity_factor=1.0, dtype="f32", bias_range=0.02),
 }

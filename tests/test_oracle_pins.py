@@ -74,6 +74,18 @@ def test_capacity_closed_form():
     # top-1: the book's (T/E)*cf is the same number
     assert oracle.capacity(16384, 1, 64, 1.25) == int(16384 / 64 * 1.25)
     assert oracle.capacity(100, 2, 8, 0.0) is None
+    assert oracle.capacity(100, 2, 8, -1.0) is None
+
+
+def test_capacity_of_dyadic_factors_is_integer_division():
+    """cf = n/64 is exact in float32, so floor(cf k T / E) is the integer quotient
+    (n k T) // (64 E): any rounding of the product, or a wrong operand, shows up on
+    some of these."""
+    for n in range(1, 400, 3):
+        for k, T, E in [(1, 16384, 64), (2, 4096, 8), (2, 250, 3), (8, 8192, 256), (3, 77, 7),
+                        (1, 1, 1), (16, 5, 512)]:
+            q = (n * k * T) // (64 * E)
+            assert oracle.capacity(T, k, E, n / 64) == max(min(q, T * k), k), (n, k, T, E)
 
 
 # --------------------------------------------------------------------------- closed forms
