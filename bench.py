@@ -7,6 +7,11 @@ grouped SwiGLU experts, combine, f/P statistics), inputs resident in HBM.  Print
 JSON line (stdout).  Besides the whole-layer rate it times each stage with HIP events on
 the launch stream (staged entry points, same kernels) to report the dominant kernel
 against its roofline, and times the CPU oracle on a bounded sample of the same batch.
+
+The headline is the Mixtral-shaped prefill layer; with the default workload the same
+line also carries timed records of the decode, fine-grained and Switch-shaped layers
+("workloads"), each with its layer time, tokens/s and the dominant kernel's roof
+fraction (--only: the named workload alone).
 """
 from __future__ import annotations
 
@@ -35,12 +40,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+
+# Layers timed beside the headline in the default run (one GPU, one after the other).
+SIDE_WORKLOADS = ("mixtral_decode", "fine_grained_shared", "switch_capacity")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (no side workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -57,15 +69,48 @@ def main():
               "MI355X (no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rec, inp, wl = run_workload(args.workload, args.steps, args.warmup, dev)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = (cpu_baseline_ec if wl.routing == "expert" else cpu_baseline)(
+            wl, inp, args.cpu_sample, rec["layer"]["flops"])
+    del inp
+    if not args.only and args.workload == "mixtral_prefill":
+        side = {}
+        for name in SIDE_WORKLOADS:
+            torch.cuda.empty_cache()
+            r, inp, _ = run_workload(name, args.steps, args.warmup, dev)
+            del inp
+            side[name] = {key: r[key] for key in ("value", "unit", "ms_per_step", "dtype",
+                                                  "config", "roofline", "layer")}
+        rec["workloads"] = side
+    print(json.dumps(rec), flush=True)
+
+    if args.copy_calibration:
+        # A plain streaming copy of known size (one elementwise dispatch that reads and
+        # writes COPY_BYTES), for scaling the HBM byte counters.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {COPY_BYTES} bytes read and written")
+
+
+def run_workload(name, steps, warmup, dev):
+    """Times `steps` moe_forward calls of workload `name` (after `warmup`), then its stages;
+    returns (record, host inputs, workload)."""
     import numpy as np
     import torch
 
     import gen
     import sparse_mixture_experts_24_amd as moe
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = gen.workload(args.workload)
+    wl = gen.workload(name)
+    args = argparse.Namespace(steps=steps, warmup=warmup)
     log(f"[bench] workload {wl.name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F} "
         f"S={wl.n_shared} cf={wl.capacity_factor} dtype={wl.dtype}")
     t0 = time.time()
@@ -203,8 +248,11 @@ def main():
     flops_gate_up = 4.0 * d * F * (N + S * T)
     flops_down = 2.0 * d * F * (N + S * T)
     flops_layer = 2.0 * T * d * E + flops_gate_up + flops_down
+    # gate/up algorithmic bytes: the touched experts' gate and up weights (+ row scales)
+    # and the token rows; H is implementation traffic (written here, read by the down
+    # GEMM) and is not counted
     w_gate_up_bytes = touched * 2.0 * F * (d * wsz + (4 if fp8 else 0))
-    bytes_gate_up = w_gate_up_bytes + T * d * esz + (N + S * T) * F * esz
+    bytes_gate_up = w_gate_up_bytes + T * d * esz
     bytes_layer = (touched * (3.0 * F * d * wsz + (4.0 * (2 * F + d) if fp8 else 0.0))
                    + E * d * esz + T * d * esz + T * d * esz)
     log(f"[bench] counts per expert: {cnt.tolist() if E <= 64 else (cnt.min(), cnt.max())}; "
@@ -239,11 +287,6 @@ def main():
         "experts_touched": touched, "stage_ms": stage_ms,
     }
 
-    # ---- CPU oracle on a bounded sample of the same batch
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = (cpu_baseline_ec if ec else cpu_baseline)(wl, inp, args.cpu_sample)
-
     rec = {
         "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -258,19 +301,13 @@ def main():
                               if nb else "token choice (top-k experts per token)"},
         "roofline": roof,
         "layer": layer,
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
     }
-    print(json.dumps(rec), flush=True)
+    log(f"[bench] {wl.name}: {T / layer_s:.4g} tokens/s, {ms:.4f} ms/step; gate/up "
+        f"{roof['achieved']:.4g} {roof['unit']} = {roof['frac']:.3f} of peak")
+    del dinp, ws, out, H, Yp, calls
+    return rec, inp, wl
 
-    if args.copy_calibration:
-        # A plain streaming copy of known size (one elementwise dispatch that reads and
-        # writes COPY_BYTES), for scaling the HBM byte counters.
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 x {COPY_BYTES} bytes read and written")
 
 
 # ---- HBM traffic of the dominant kernel, from rocprofv3 counters
@@ -342,37 +379,72 @@ def summarize_pmc(workload, fetch_csv, write_csv):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(wl, inp, sample):
+def host_info():
+    """Threads the oracle's BLAS uses, the cores this process may run on, and the CPU model."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        blas = os.cpu_count()
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return int(blas), int(nproc), int(os.cpu_count() or 0), model
+
+
+def timed_runs(fn, runs=3):
+    """One untimed warm-up call, then the median wall time of `runs` calls."""
+    import statistics
+    fn()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts), ts
+
+
+def cpu_baseline(wl, inp, sample, layer_flops):
     """The oracle, as it stands, on the host cores: routing + dispatch of the whole batch
-    plus the experts of a sample of tokens, scaled to the whole batch."""
+    plus the experts of an evenly spaced sample of tokens, scaled to the whole batch.
+    Protocol: one warm-up, then the median of three runs of each part."""
     import numpy as np
 
     import oracle
     from oracle import moe_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        cores = os.cpu_count()
+    blas, nproc, ncpu, model = host_info()
     if not sample:
         per_tok = 6.0 * wl.d * wl.F * (wl.k + wl.n_shared)
-        sample = int(max(8, min(wl.T, 6.0e12 / per_tok)))   # ~10-20 s of oracle work
-    t0 = time.perf_counter()
+        sample = int(max(8, min(wl.T, 2.0e12 / per_tok)))   # ~2-4 s of oracle work per run
     x = mo._np(inp["x"])
-    r = oracle.route(x, mo._np(inp["W_router"]), wl.k, mo._np(inp["router_bias"]))
+    Wr, b = mo._np(inp["W_router"]), mo._np(inp["router_bias"])
     C = oracle.capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
-    disp = oracle.dispatch(r["idx"], wl.E, C)
-    oracle.aux_stats(r["p"], r["idx"], wl.E)
-    t_route = time.perf_counter() - t0
+    state = {}
+
+    def route_part():
+        r = oracle.route(x, Wr, wl.k, b)
+        state["r"] = r
+        state["disp"] = oracle.dispatch(r["idx"], wl.E, C)
+        oracle.aux_stats(r["p"], r["idx"], wl.E)
+
+    t_route, _ = timed_runs(route_part)
     rows = np.linspace(0, wl.T - 1, sample).astype(np.int64)
-    t1 = time.perf_counter()
-    oracle.forward_rows(inp, rows, wl.k, wl.capacity_factor, wl.n_shared,
-                        h_bf16=(wl.dtype == "bf16"), routing=r, disp=disp)
-    t_exp = time.perf_counter() - t1
+    t_exp, ts = timed_runs(lambda: oracle.forward_rows(
+        inp, rows, wl.k, wl.capacity_factor, wl.n_shared, h_bf16=(wl.dtype == "bf16"),
+        routing=state["r"], disp=state["disp"]))
     full = t_route + t_exp * wl.T / rows.size
     log(f"[bench] oracle: route+dispatch {t_route:.2f}s for {wl.T} tokens, experts "
-        f"{t_exp:.2f}s for {rows.size} tokens -> {full:.1f}s per batch")
-    return {"value": wl.T / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        f"{t_exp:.2f}s (median of {[round(t, 2) for t in ts]}) for {rows.size} tokens -> "
+        f"{full:.1f}s per batch; {blas} BLAS threads, nproc {nproc}, {model}")
+    return {"value": wl.T / full, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "gflops": layer_flops / full / 1e9, "nproc": nproc, "cpu_count": ncpu,
+            "cpu_model": model, "runs": "1 warm-up + median of 3",
             "sample": f"routing+dispatch of all {wl.T} tokens ({t_route:.2f}s) + experts of "
                       f"{rows.size} evenly spaced tokens ({t_exp:.2f}s), scaled to the batch"}
 
@@ -421,42 +493,48 @@ def expert_choice_stages(moe, L, desc, dinp, ws, out2, f, p, P, sp, dev):
     return st
 
 
-def cpu_baseline_ec(wl, inp, sample):
+def cpu_baseline_ec(wl, inp, sample, layer_flops):
     """The oracle on the host for an expert-choice layer: probabilities and the per-expert
     selection of the whole batch, plus the experts of a sample of tokens (each through
-    every expert that took it), scaled to the whole batch."""
+    every expert that took it), scaled to the whole batch.  One warm-up, then the median
+    of three runs of each part."""
     import numpy as np
 
     import oracle
     from oracle import moe_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        cores = os.cpu_count()
+    blas, nproc, ncpu, model = host_info()
     if not sample:
         per_tok = 6.0 * wl.d * wl.F * (wl.k + wl.n_shared)
-        sample = int(max(8, min(wl.T, 6.0e12 / per_tok)))
-    t0 = time.perf_counter()
+        sample = int(max(8, min(wl.T, 2.0e12 / per_tok)))
     x = mo._np(inp["x"])
-    probs = oracle.router_probs(x, mo._np(inp["W_router"]))
     C = oracle.expert_choice_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
-    sel, _ = oracle.expert_choice_select(probs, C)
-    t_route = time.perf_counter() - t0
+    state = {}
+
+    def route_part():
+        state["probs"] = oracle.router_probs(x, mo._np(inp["W_router"]))
+        state["sel"], _ = oracle.expert_choice_select(state["probs"], C)
+
+    t_route, _ = timed_runs(route_part)
     rows = np.linspace(0, wl.T - 1, sample).astype(np.int64)
-    t1 = time.perf_counter()
     hb = wl.dtype == "bf16"
-    y = np.zeros((rows.size, wl.d))
-    for e in range(wl.E):
-        hit = np.nonzero(np.isin(rows, sel[e]))[0]
-        if hit.size:
-            o = oracle.expert_ffn(x[rows[hit]], *oracle.expert_weights(inp, e), hb)
-            y[hit] += probs[rows[hit], e].astype(np.float64)[:, None] * o
-    t_exp = time.perf_counter() - t1
+
+    def expert_part():
+        probs, sel = state["probs"], state["sel"]
+        y = np.zeros((rows.size, wl.d))
+        for e in range(wl.E):
+            hit = np.nonzero(np.isin(rows, sel[e]))[0]
+            if hit.size:
+                o = oracle.expert_ffn(x[rows[hit]], *oracle.expert_weights(inp, e), hb)
+                y[hit] += probs[rows[hit], e].astype(np.float64)[:, None] * o
+        return y
+
+    t_exp, ts = timed_runs(expert_part)
     full = t_route + t_exp * wl.T / rows.size
     log(f"[bench] oracle: probabilities+selection {t_route:.2f}s for {wl.T} tokens, experts "
         f"{t_exp:.2f}s for {rows.size} tokens -> {full:.1f}s per batch")
-    return {"value": wl.T / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": wl.T / full, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "gflops": layer_flops / full / 1e9, "nproc": nproc, "cpu_count": ncpu,
+            "cpu_model": model, "runs": "1 warm-up + median of 3",
             "sample": f"probabilities and expert-choice selection of all {wl.T} tokens "
                       f"({t_route:.2f}s) + experts of {rows.size} evenly spaced tokens "
                       f"({t_exp:.2f}s), scaled to the batch"}

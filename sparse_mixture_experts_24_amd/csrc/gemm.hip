@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "moe_internal.h"
 
@@ -1046,24 +1047,42 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Facts about the current device, looked up once per device (the library may drive
+// several GPUs from several threads).
+constexpr int kMaxDevices = 64;
+
 static int device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::atomic<int> cached[kMaxDevices];   // 0: not looked up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
+    n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// The grouped GEMM kernels take more dynamic LDS than the default limit: raised once per
+// device and kernel (a repeated call from a racing thread sets the same value again).
+template <bool GATED, bool FP8>
+static hipError_t allow_kernel_lds() {
+  static std::atomic<bool> done[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED, FP8>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)KERNEL_LDS_BYTES);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
+  return hipSuccess;
 }
 
 template <bool GATED, bool FP8>
 static hipError_t run_bf16(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<GATED, FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)KERNEL_LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = allow_kernel_lds<GATED, FP8>();
+  if (e != hipSuccess) return e;
   int64_t grid = device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   grid = round_up(grid, 8);

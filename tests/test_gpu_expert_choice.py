@@ -16,8 +16,8 @@ import gen
 import oracle
 import sparse_mixture_experts_24_amd as moe
 from gen import Workload
-from parity import (STAT_TOL, check_expert_choice, check_y, check_y_rounding_aware,
-                    expert_choice_rows_reference, np32, to_dev)
+from parity import (STAT_TOL, check_expert_choice, check_full_layer, check_y,
+                    check_y_rounding_aware, expert_choice_rows_reference, np32, to_dev)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -197,19 +197,14 @@ def test_expert_choice_full_size():
     torch.cuda.synchronize()
     H = H.float().cpu().numpy()
     del xpad
-    rng = np.random.default_rng(0)
     taken = np.zeros(wl.T, np.int64)
     for e in range(wl.E):
         taken[sel[e]] += 1
-    rows = {0, wl.T - 1, int(np.argmax(taken))}
-    rows.update(rng.choice(wl.T, 12, replace=False).tolist())
-    untaken = np.nonzero(taken == 0)[0]
-    rows.update(untaken[:2].tolist())
-    rows = np.array(sorted(rows))
-    print(f"[full ec] oracle experts for {rows.size} rows ({untaken.size} untaken tokens)",
-          flush=True)
-    y_ref, items = expert_choice_rows_reference(inp, rows, sel, p_ref, 0, True)
-    nflip = check_y_rounding_aware(y.float().cpu().numpy()[rows], y_ref, items, H, True, True,
-                                   "full expert choice: sampled rows")
-    print(f"[full ec] {nflip} of {y_ref.size} sampled elements needed the bf16-rounding "
-          f"allowance", flush=True)
+    print(f"[full ec] oracle experts for all {wl.T} rows ({int((taken == 0).sum())} untaken "
+          f"tokens)", flush=True)
+    groups = [(e, e * C, (e + 1) * C, sel[e].astype(np.int64)) for e in range(wl.E)]
+    nallow, flips = check_full_layer(y.float().cpu().numpy(), inp, groups, wl.T, wl.d, p_ref,
+                                     slot.cpu().numpy().reshape(-1), True, True, H, wl.E * C,
+                                     None, "full expert choice: all rows")
+    print(f"[full ec] {nallow} of {wl.T * wl.d} output elements needed the bf16-rounding "
+          f"allowance; {flips} h values on the other side of a midpoint", flush=True)

@@ -1,10 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench times
 (MoELayer.__call__ -> moe_forward with a reused workspace).
 
-The oracle routes and dispatches every token (cheap) and runs the experts for a sample
-of output rows, one by one.  Routing is bit-exact outside near-ties, dispatch is
-bit-exact under the oracle's routing, f and P agree to 1e-5, and the sampled rows of y
-satisfy the output rule.
+The oracle routes and dispatches every token and runs every expert on all of its rows.
+Routing is bit-exact outside near-ties, dispatch is bit-exact under the oracle's
+routing, f and P agree to 1e-5, and every row of y satisfies the output rule (with the
+validated bf16-rounding allowance for h, counted and bounded).
 """
 import numpy as np
 import pytest
@@ -13,25 +13,13 @@ import torch
 import gen
 import oracle
 import sparse_mixture_experts_24_amd as moe
-from parity import (STAT_TOL, check_routing, check_y_rounding_aware, expert_rows_reference,
-                    np32, to_dev)
+from parity import STAT_TOL, check_full_layer, check_routing, np32, to_dev, token_choice_groups
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 FULL = ["tiny_f32", "mixtral_decode", "mixtral_prefill", "switch_capacity", "fine_grained_shared",
         "mixtral_decode_fp8", "switch_capacity_fp8"]
-
-
-def sample_rows(T, n, slot_pos, k, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set([0, T - 1])
-    rows.update(rng.choice(T, min(T, n), replace=False).tolist())
-    sp = slot_pos.reshape(T, k)
-    dropped = np.nonzero(np.all(sp < 0, axis=1))[0]
-    if dropped.size:                      # include fully dropped tokens (output 0)
-        rows.update(dropped[:4].tolist())
-    return np.array(sorted(rows))
 
 
 @pytest.mark.timeout(900)
@@ -99,19 +87,19 @@ def test_full_size(name):
     H = H.float().cpu().numpy()
     del Yp, y_staged
 
-    # sampled output rows, with the layer's own (validated) routing
-    routing = dict(r, idx=idx, w=oracle.renorm_weights(r["p"], idx))
+    # every output row, with the layer's own (validated) routing
+    w_ref = oracle.renorm_weights(r["p"], idx)
     d_gpu = oracle.dispatch(idx, wl.E, C)
     assert np.array_equal(slot_g.cpu().numpy(), d_gpu["slot_pos"])
-    rows = sample_rows(wl.T, 16 if wl.T > 64 else wl.T, d_gpu["slot_pos"], wl.k)
-    print(f"[full] {name}: oracle experts for {rows.size} rows", flush=True)
     hb = wl.dtype == "bf16"
-    y_ref = oracle.forward_rows(inp, rows, wl.k, wl.capacity_factor, wl.n_shared,
-                                h_bf16=hb, routing=routing, disp=d_gpu)
-    y_ref2, items = expert_rows_reference(inp, rows, wl.k, wl.n_shared, hb, routing, d_gpu)
-    np.testing.assert_allclose(y_ref2, y_ref, rtol=1e-6, atol=1e-7)
-    nflip = check_y_rounding_aware(y[rows], y_ref, items, H, hb, hb, f"{name}: sampled rows")
-    print(f"[full] {name}: {nflip} of {y_ref.size} sampled elements needed the bf16-rounding "
-          f"allowance of the per-element rule", flush=True)
+    print(f"[full] {name}: oracle experts for all {wl.T} rows", flush=True)
+    groups = token_choice_groups(d_gpu["offsets"], d_gpu["perm_src"], wl.k, wl.E, wl.n_shared,
+                                 wl.T)
+    nallow, flips = check_full_layer(y, inp, groups, wl.T, wl.d, w_ref, d_gpu["slot_pos"], hb,
+                                     hb, H, wl.T * wl.k + wl.n_shared * wl.T,
+                                     wl.T * wl.k if wl.n_shared else None, f"{name}: all rows")
+    print(f"[full] {name}: {nallow} of {y.size} output elements needed the bf16-rounding "
+          f"allowance of the per-element rule; {flips} h values rounded to the other "
+          f"neighbour of a midpoint", flush=True)
     del dinp, layer
     torch.cuda.empty_cache()

@@ -14,8 +14,8 @@ import gen
 import oracle
 import sparse_mixture_experts_24_amd as moe
 from gen import Workload
-from parity import (STAT_TOL, check_candidates, check_routing, check_y,
-                    check_y_rounding_aware, expert_rows_reference, np32, to_dev)
+from parity import (STAT_TOL, check_candidates, check_full_layer, check_routing, check_y, np32,
+                    to_dev, token_choice_groups)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -184,24 +184,14 @@ def test_next_best_full_size():
     torch.cuda.synchronize()
     H = H.float().cpu().numpy()
     del Yp
-    routing = dict(r, idx=idx_n, w=oracle.renorm_weights(r["p"], idx_n))
-    rng = np.random.default_rng(0)
-    moved = np.nonzero((d_ref["expert"] >= 0) & (d_ref["expert"] != idx_n.reshape(-1)))[0]
-    dropped = np.nonzero(d_ref["slot_pos"] < 0)[0]
-    rows = {0, wl.T - 1}
-    rows.update(rng.choice(wl.T, 10, replace=False).tolist())
-    rows.update((moved[:4] // wl.k).tolist())
-    rows.update((dropped[:2] // wl.k).tolist())
-    rows = np.array(sorted(rows))
-    print(f"[full nb] oracle experts for {rows.size} rows", flush=True)
-    y_ref = oracle.forward_rows(inp, rows, wl.k, wl.capacity_factor, wl.n_shared, h_bf16=True,
-                                routing=routing, disp=d_ref)
-    d_rows = dict(d_ref)
-    y_ref2, items = expert_rows_reference(inp, rows, wl.k, wl.n_shared, True,
-                                          dict(routing, idx=d_ref["expert"].reshape(wl.T, wl.k)),
-                                          d_rows)
-    np.testing.assert_allclose(y_ref2, y_ref, rtol=1e-6, atol=1e-7)
-    nflip = check_y_rounding_aware(y.float().cpu().numpy()[rows], y_ref, items, H, True, True,
-                                   "full next-best: sampled rows")
-    print(f"[full nb] {nflip} of {y_ref.size} sampled elements needed the bf16-rounding "
-          f"allowance", flush=True)
+    w_ref = oracle.renorm_weights(r["p"], idx_n)
+    print(f"[full nb] oracle experts for all {wl.T} rows", flush=True)
+    groups = token_choice_groups(d_ref["offsets"], d_ref["perm_src"], wl.k, wl.E, wl.n_shared,
+                                 wl.T)
+    nallow, flips = check_full_layer(y.float().cpu().numpy(), inp, groups, wl.T, wl.d, w_ref,
+                                     d_ref["slot_pos"], True, True, H,
+                                     wl.T * wl.k + wl.n_shared * wl.T,
+                                     wl.T * wl.k if wl.n_shared else None,
+                                     "full next-best: all rows")
+    print(f"[full nb] {nallow} of {wl.T * wl.d} output elements needed the bf16-rounding "
+          f"allowance; {flips} h values on the other side of a midpoint", flush=True)
