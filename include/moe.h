@@ -59,7 +59,9 @@ typedef enum {
   MOE_E_SHAPE = 2,        /* inconsistent or out-of-range sizes */
   MOE_E_UNSUPPORTED = 3,  /* valid layer, but outside what the kernels implement */
   MOE_E_WORKSPACE = 4,    /* workspace NULL or smaller than moe_workspace_bytes */
-  MOE_E_HIP = 5           /* a HIP launch failed */
+  MOE_E_HIP = 5,          /* a HIP launch failed */
+  MOE_E_SCRATCH = 6       /* moe_forward_noalloc: the layer needs more scratch than the
+                             library's static device buffer holds */
 } moe_status_t;
 
 /* Layer description shared by every entry point.
@@ -278,6 +280,27 @@ moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
                                        const void* W_up, const void* W_down, void* out, float* f,
                                        float* p, void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/* ---- Allocation-free entry point.
+ * For callers that cannot allocate device memory or call hipMalloc at all: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same layer and
+ * arguments as moe_forward, without the workspace: its scratch is a static device buffer
+ * inside the library, MOE_NOALLOC_SCRATCH_BYTES per GPU, that each GPU the library is
+ * loaded on holds until the process ends.  The caller still passes inputs and outputs.
+ *   - A layer whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ *     MOE_E_SCRATCH and enqueues nothing (decode-sized and small prefill batches fit:
+ *     e.g. T 16 of a d 4096, d_ff 14336, top-2 layer needs about 2 MB).
+ *   - Every call on one GPU uses that GPU's single buffer: calls that overlap on one GPU
+ *     (other streams, other threads) race and must be ordered by the caller.  The buffer
+ *     keeps the last call's contents; each call clears what it needs at zero by kernel.
+ *   - The first call on each device looks the buffer's address up (a host query, no
+ *     allocation); make it outside graph capture.
+ *   - Calls no hipMalloc, hipFree or other allocating routine. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const moe_desc_t* desc, const void* x, const void* W_router,
+                                 const float* router_bias, const void* W_gate, const void* W_up,
+                                 const void* W_down, void* out, float* f, float* p,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,14 +27,17 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_UNSUPPORTED",
-          4: "MOE_E_WORKSPACE", 5: "MOE_E_HIP"}
+          4: "MOE_E_WORKSPACE", 5: "MOE_E_HIP", 6: "MOE_E_SCRATCH"}
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_capacity",
            "moe_forward", "moe_route", "moe_dispatch", "moe_experts", "moe_experts_gate_up",
            "moe_experts_down", "moe_combine", "moe_forward_fp8", "moe_experts_fp8",
            "moe_experts_gate_up_fp8", "moe_experts_down_fp8",
            "moe_workspace_bytes_expert_choice", "moe_capacity_expert_choice",
            "moe_route_expert_choice", "moe_combine_expert_choice", "moe_forward_expert_choice",
-           "moe_forward_next_best", "moe_route_next_best", "moe_dispatch_next_best")
+           "moe_forward_next_best", "moe_route_next_best", "moe_dispatch_next_best",
+           "moe_forward_noalloc")
+# Bytes of the library's static device scratch that moe_forward_noalloc uses (moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeDesc(ctypes.Structure):
@@ -112,6 +115,8 @@ def lib():
         L.moe_route_next_best.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_dispatch_next_best.restype = I
         L.moe_dispatch_next_best.argtypes = [D, P, P, P, P, P, P, P, S, P]
+        L.moe_forward_noalloc.restype = I
+        L.moe_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -214,6 +219,34 @@ def forward(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor=0
                            _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(out), _ptr(f), _ptr(p),
                            _ptr(ws), ws.numel(), _stream(dev))
     _check("moe_forward", st)
+    return out, f, p
+
+
+def forward_noalloc(x, W_router, router_bias, W_gate, W_up, W_down, k, capacity_factor=0.0, *,
+                    out, f=None, p=None, out_dtype=None):
+    """The whole layer through moe_forward_noalloc: no workspace, the library's static
+    device scratch instead (NOALLOC_SCRATCH_BYTES per GPU; larger layers raise with
+    MOE_E_SCRATCH).  `out` (and f, p, if wanted) must be given, so that nothing is
+    allocated here either.  Calls that overlap on one GPU race on that scratch."""
+    dev = x.device
+    desc = desc_for(x, W_router, W_gate, k, capacity_factor, out_dtype)
+    T, d = x.shape
+    E = W_router.shape[0]
+    G, F, _ = W_gate.shape
+    for t, n, shp in ((x, "x", (T, d)), (W_router, "W_router", (E, d)),
+                      (W_gate, "W_gate", (G, F, d)), (W_up, "W_up", (G, F, d)),
+                      (W_down, "W_down", (G, d, F))):
+        _require(t, n, dev, x.dtype, shp)
+    _require(router_bias, "router_bias", dev, torch.float32, (E,))
+    if out is None:
+        raise ValueError("forward_noalloc needs the output tensor `out`")
+    _require(out, "out", dev, out_dtype or x.dtype, (T, d))
+    _require(f, "f", dev, torch.float32, (E,))
+    _require(p, "p", dev, torch.float32, (E,))
+    st = lib().moe_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(W_router),
+                                   _ptr(router_bias), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+                                   _ptr(out), _ptr(f), _ptr(p), _stream(dev))
+    _check("moe_forward_noalloc", st)
     return out, f, p
 
 

@@ -1049,7 +1049,6 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
 
 // Facts about the current device, looked up once per device (the library may drive
 // several GPUs from several threads).
-constexpr int kMaxDevices = 64;
 
 static int device_cu_count() {
   static std::atomic<int> cached[kMaxDevices];   // 0: not looked up yet

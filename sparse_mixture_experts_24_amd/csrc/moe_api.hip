@@ -4,6 +4,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -331,6 +333,8 @@ const char* moe_status_str(moe_status_t s) {
     case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: outside what the kernels implement";
     case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_E_HIP: return "MOE_E_HIP: a HIP launch failed";
+    case MOE_E_SCRATCH:
+      return "MOE_E_SCRATCH: the layer needs more scratch than the static device buffer holds";
   }
   return "unknown moe_status_t";
 }
@@ -626,3 +630,49 @@ moe_status_t moe_dispatch_next_best(const moe_desc_t* desc, const int32_t* topk_
 }
 
 }  // extern "C"
+
+// ---- allocation-free entry point
+namespace moe {
+
+// The scratch of moe_forward_noalloc.  On the host `scratch` names a stand-in, not device
+// memory: host code never passes it to a kernel, a memset or a copy; it uses the address
+// hipGetSymbolAddress returns for the current device (each GPU holds its own copy).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static std::atomic<void*> scratch_addr[kMaxDevices];
+static std::mutex scratch_mu;
+
+// Device address of the current device's scratch, looked up on its first use.
+static moe_status_t device_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_E_UNSUPPORTED;
+  void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return MOE_E_HIP;
+      scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" moe_status_t moe_forward_noalloc(const moe_desc_t* desc, const void* x,
+                                            const void* W_router, const float* router_bias,
+                                            const void* W_gate, const void* W_up,
+                                            const void* W_down, void* out, float* f, float* p,
+                                            void* stream) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (carve_workspace(*desc, nullptr).bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_E_SCRATCH;
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws)) != MOE_OK) return st;
+  return forward_impl(desc, x, W_router, router_bias, plain_weights(W_gate, W_up, W_down), out,
+                      f, p, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

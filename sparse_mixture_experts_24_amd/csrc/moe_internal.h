@@ -13,6 +13,9 @@ typedef uint16_t bf16_t;
 // Upper limits enforced by moe_validate.
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
+// Devices whose per-device facts (CU count, kernel attributes, static scratch address) the
+// library caches.
+constexpr int kMaxDevices = 64;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

@@ -79,7 +79,7 @@ def test_validate(L, kw, status):
 
 
 def test_status_strings(L):
-    for code in range(6):
+    for code in range(7):
         assert L.moe_status_str(code).decode().startswith(moe.STATUS[code])
 
 
