@@ -22,11 +22,12 @@ static moe_status_t validate(const moe_desc_t* d) {
   if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_E_UNSUPPORTED;
   if (d->d_model % 64 || d->d_ff % 64 || d->d_model > 65536 || d->d_ff > 65536)
     return MOE_E_UNSUPPORTED;
+  // 32-bit element offsets inside the kernels.  T is bounded first, so that with every
+  // other field already bounded above none of the products below can overflow.
+  if (d->T > (int64_t)INT32_MAX / 32) return MOE_E_UNSUPPORTED;
   const int64_t rows = d->T * d->top_k + d->n_shared * d->T;
-  // 32-bit element offsets inside the kernels
-  if (d->T > (int64_t)INT32_MAX / 32 || rows > (int64_t)INT32_MAX ||
-      d->T * d->d_model > (int64_t)INT32_MAX || rows * d->d_ff > (int64_t)INT32_MAX ||
-      d->d_ff * d->d_model > (int64_t)INT32_MAX)
+  if (rows > (int64_t)INT32_MAX || d->T * d->d_model > (int64_t)INT32_MAX ||
+      rows * d->d_ff > (int64_t)INT32_MAX || d->d_ff * d->d_model > (int64_t)INT32_MAX)
     return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
