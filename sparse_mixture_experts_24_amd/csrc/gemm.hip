@@ -46,6 +46,7 @@ struct GemmArgs {
   int64_t shared_row0;    // T*k: first row of the shared expert
   int T, topk, E, G, N, K, n_tiles;
   int narrow_small;       // small groups take half-width tiles (gate/up 64, down 128 columns)
+  int skinny_all;         // every group has at most 32 rows (static order: streamed tiles)
   int* ctr;               // NULL, or 8 per-XCD unit counters, zero at launch
   const float* sc0;       // 8-bit weights: per-row scales of B0 [G, N] (else unused)
   const float* sc1;       // 8-bit weights: per-row scales of B1 (gated)
@@ -269,12 +270,13 @@ constexpr size_t SMALL_LDS_BYTES =
 // Steps of weights in flight per wave (measured on decode-sized launches: about 16 KB
 // (two-block tiles) to 32 KB (one-block down tiles) per wave is best; more is slower).
 constexpr int STREAM_P2 = 2, STREAM_P1 = 8;
-// Tiles whose group has at most 32 rows left take the barrier-free skinny tile, with 2
-// (bf16 weights) or 4 (8-bit weights: half the bytes per step) K steps in flight per wave
-// (measured on decode-sized launches; deeper is slower).
+// Tiles whose group has at most 32 rows left take the barrier-free skinny tile, with 4 K
+// steps of weights and tokens in flight per wave.  (Measured on decode-sized launches: with
+// each tile drained before the next one, 2 steps were best for bf16 weights; with the tiles
+// of a launch streamed back to back, 4 steps take the Mixtral decode gate/up from 0.332 to
+// 0.309 ms and the 8-bit one from 0.217 to 0.194 ms; 6 or 8 steps are no faster.)
 constexpr int SKINNY_ROWS = 32;
-template <bool FP8>
-constexpr int skinny_p() { return FP8 ? 4 : 2; }
+constexpr int SKINNY_P = 4;
 constexpr size_t KERNEL_LDS_BYTES =
     GEMM_LDS_BYTES > SMALL_LDS_BYTES ? GEMM_LDS_BYTES : SMALL_LDS_BYTES;
 // 8-bit weights: a K step of a row is 64 bytes, read by 4 lanes (16 rows per load); the
@@ -423,21 +425,42 @@ __device__ __forceinline__ void gemm_bf16_tile_stream(const GemmArgs& a, bf16_t*
   store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
 }
 
-// A tile of at most 32 rows (decode-sized groups): every wave computes all of them against
-// its own weight rows and reads its token fragments straight from global memory (the few
-// rows are L1/L2 hits), so the K loop has no block barrier and no LDS traffic for the
+// Coordinates of one tile of the table: group, its rows, the tile's first row and column,
+// and its K rotation.
+struct TileAt {
+  int g, M, m0, ncol0, rot;
+  int64_t row_begin;
+};
+
+// One tile, as a sequence of length one for gemm_skinny_stream.
+struct OneTile {
+  TileAt t;
+  __device__ bool get(int r, TileAt& out) const {
+    out = t;
+    return r == 0;
+  }
+};
+
+// Tiles of at most 32 rows (decode-sized groups): every wave computes all of the tile's rows
+// against its own weight rows and reads its token fragments straight from global memory (the
+// few rows are L1/L2 hits), so the K loop has no block barrier and no LDS traffic for the
 // tokens.  The weights stream as in gemm_bf16_tile_stream (whole row segments per load,
 // through the wave's swizzled LDS stages); P steps of weights and tokens are in flight.
+//
+// The block walks a sequence of such tiles (units.get(r, tile) for r = 0, 1, ... while it
+// returns true) as one stream: the loads of a tile's last P steps are those of the next
+// tile's first P steps, so the pipeline does not drain between tiles and each tile's
+// epilogue overlaps the next tile's first loads.  (Each tile takes nkp = nk rounded up to P
+// steps; steps past nk multiply zero token fragments.)  The epilogue's LDS transpose sits
+// past the four waves' weight stages, which hold the next tile's first step meanwhile.
 //
 // Gate/up with NB == 1 (64-column tiles, for launches whose tiles would leave much of a
 // last round idle): the wave's 32 weight rows are 16 gate rows and the 16 matching up rows
 // and the MFMA is taken transposed (D[weight row][token]), so a lane holds gate and up of
 // one (token, h) in registers r and r + 8.
-template <int NB, bool GATED, int P, bool FP8>
-__device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t* smem, int g,
-                                                      int64_t row_begin, int M, int m0,
-                                                      int ncol0, int k0, int nk, int rot,
-                                                      void* outp) {
+template <int NB, bool GATED, int P, bool FP8, typename Units>
+__device__ __forceinline__ void gemm_skinny_stream(const GemmArgs& a, bf16_t* smem,
+                                                   const Units& units) {
   constexpr bool PAIRED = GATED && NB == 1;
   static_assert(P % 2 == 0, "the step loop is unrolled by P (even: two LDS stages)");
   constexpr int MB = 1;
@@ -445,39 +468,45 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
   constexpr int WB = FP8 ? 1 : 2;               // bytes per weight
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int fr = lane & 31, fg = lane >> 5;
-  const bf16_t* A = (const bf16_t*)a.A + k0 * BK;
-  const int K = a.K, N = a.N;
+  const bf16_t* A = (const bf16_t*)a.A;
+  const int K = a.K, N = a.N, nk = K / BK, nkp = (nk + P - 1) / P * P;
   bf16_t* Bw = smem + w * 2 * SB_STAGE;          // this wave's two B stages
+  bf16_t* Ht = smem + 4 * 2 * SB_STAGE;          // epilogue transpose, past every wave's stages
 
-  // token row of this lane's fragments: row fr of the tile (rows past M read row 0 of the
-  // group; their results are never stored); lane half fg reads k 32 fg .. 32 fg + 31
-  int aoff;
-  {
-    const int m = m0 + fr < M ? m0 + fr : 0;
-    if (GATED && g < a.E) aoff = a.perm_src[row_begin + m] / a.topk * K;
-    else aoff = ((GATED ? 0 : (int)row_begin) + m) * K;
-    aoff += 32 * fg;
-  }
-  const char* pbl[NL];
-  int bst[NL];
-  int bcol[NB];
+  // Per-tile addressing: the lane's token row (row fr of the tile; rows past M read row 0
+  // of the group, their results are never stored; lane half fg reads k 32 fg .. 32 fg + 31)
+  // and its weight row segments.
+  struct Addr {
+    const char* pbl[NL];
+    int aoff, rot;
+  };
+  auto addr_of = [&](const TileAt& u, Addr& ad) {
+    const int m = u.m0 + fr < u.M ? u.m0 + fr : 0;
+    if (GATED && u.g < a.E) ad.aoff = a.perm_src[u.row_begin + m] / a.topk * K;
+    else ad.aoff = ((GATED ? 0 : (int)u.row_begin) + m) * K;
+    ad.aoff += 32 * fg;
+    ad.rot = u.rot;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int nb = FP8 ? j / 2 : j / 4;
+      const int r = FP8 ? 16 * (j % 2) + (lane >> 2) : 8 * (j % 4) + (lane >> 3);
+      const int c = FP8 ? lane & 3 : lane & 7;
+      const int n = PAIRED  ? u.ncol0 + 16 * w + (r & 15)
+                    : GATED ? u.ncol0 + 32 * w + r
+                            : u.ncol0 + 32 * NB * w + 32 * nb + r;
+      const char* base = (const char*)((PAIRED ? r >= 16 : (GATED && nb == 1)) ? a.B1 : a.B0);
+      ad.pbl[j] = base + (((int64_t)u.g * N + min(n, N - 1)) * K) * WB + 16 * c;
+    }
+  };
+  int bst[NL];   // byte offset of each B load in the wave's stage
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    const int nb = FP8 ? j / 2 : j / 4;
     const int r = FP8 ? 16 * (j % 2) + (lane >> 2) : 8 * (j % 4) + (lane >> 3);
     const int c = FP8 ? lane & 3 : lane & 7;
-    const int n = PAIRED  ? ncol0 + 16 * w + (r & 15)
-                  : GATED ? ncol0 + 32 * w + r
-                          : ncol0 + 32 * NB * w + 32 * nb + r;
-    const char* base =
-        (const char*)((PAIRED ? r >= 16 : (GATED && nb == 1)) ? a.B1 : a.B0);
-    pbl[j] = base + (((int64_t)g * N + min(n, N - 1)) * K + k0 * BK) * WB + 16 * c;
+    const int nb = FP8 ? j / 2 : j / 4;
     bst[j] = FP8 ? (nb * 32 + r) * BK + 16 * (c ^ ((r >> 2) & 3))
                  : 2 * ((nb * 32 + r) * BK + 8 * (c ^ ((r >> 1) & 7)));
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    bcol[nb] = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
   int brd[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -485,29 +514,27 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
                  : 2 * (fr * BK + 8 * ((4 * fg + s) ^ ((fr >> 1) & 7)));
 
   floatx16 acc[MB][NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[0][j][r] = 0.0f;
-
   u32x4 rb[P][NL];       // weights of steps in flight: set q holds step t with t % P == q
   bf16x8 ra[P][4];       // token fragments of the same steps (k16 steps 0..3)
 
-#define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
-#define MOE_KLOAD(q, t)                                                                    \
+  // Tile step t reads K step (t + rot) mod nk (see k_rotation); steps past nk are clamped.
+#define MOE_KROT(ad, t) ((min((t), nk - 1) + (ad).rot) - ((min((t), nk - 1) + (ad).rot) >= nk ? nk : 0))
+#define MOE_KLOAD(q, ad, t)                                                                \
   {                                                                                        \
+    const int ks_ = MOE_KROT(ad, t);                                                       \
     _Pragma("unroll") for (int j = 0; j < NL; ++j)                                         \
-      rb[q][j] = *reinterpret_cast<const u32x4*>(pbl[j] + MOE_KSTEP(t) * BK * WB);         \
+      rb[q][j] = *reinterpret_cast<const u32x4*>((ad).pbl[j] + ks_ * BK * WB);             \
     _Pragma("unroll") for (int s = 0; s < 4; ++s)                                          \
-      ra[q][s] = *reinterpret_cast<const bf16x8*>(A + aoff + MOE_KSTEP(t) * BK + 8 * s);   \
+      ra[q][s] = *reinterpret_cast<const bf16x8*>(A + (ad).aoff + ks_ * BK + 8 * s);       \
   }
 #define MOE_KSTORE_B(q, st)                                                                \
   _Pragma("unroll") for (int j = 0; j < NL; ++j)                                           \
     *reinterpret_cast<u32x4*>((char*)Bw + (st) * SB_STAGE * 2 + bst[j]) = rb[q][j];
-  // K step t (weights in stage t % 2, tokens in set t % P): the weights of step t+1 go from
-  // their registers into the other stage and the set is refilled with step t+1+P.  Steps
-  // t >= nk (padding to a multiple of P) multiply zero token fragments.
-#define MOE_KSTEP_BODY(t, q0, q1)                                                          \
+  // Tile step t (weights in stage t % 2, tokens in set t % P): the weights of step t+1 go
+  // from their registers into the other stage, and the set is refilled with step lt of the
+  // tile whose addresses are ad (step t+P of this tile, or step t+P-nkp of the next).
+  // Steps t >= nk multiply zero token fragments.
+#define MOE_KSTEP_BODY(t, q0, q1, ad, lt)                                                  \
   {                                                                                        \
     MOE_KSTORE_B(q1, ((t) + 1) & 1);                                                       \
     const char* Bs_ = (const char*)Bw + ((t) & 1) * SB_STAGE * 2;                          \
@@ -531,65 +558,91 @@ __device__ __forceinline__ void gemm_bf16_tile_skinny(const GemmArgs& a, bf16_t*
                                                                0);                         \
       }                                                                                    \
     }                                                                                      \
-    MOE_KLOAD(q0, (t) + P);                                                                \
+    MOE_KLOAD(q0, ad, lt);                                                                 \
   }
 
-  // Prologue: steps 0..P-1 requested; step 0's weights stored.  Step t's set q0 = t % P is
-  // reloaded with step t+P after its MFMAs; set q1 = (t+1) % P was requested P-1 steps ago.
+  TileAt cur;
+  if (!units.get(0, cur)) return;
+  Addr ac;
+  addr_of(cur, ac);
+  // Prologue: steps 0..P-1 of the first tile requested; step 0's weights stored.
 #pragma unroll
-  for (int q = 0; q < P; ++q) MOE_KLOAD(q, q);
+  for (int q = 0; q < P; ++q) MOE_KLOAD(q, ac, q);
   MOE_KSTORE_B(0, 0);
-  const int nkp = (nk + P - 1) / P * P;
-  for (int kt = 0; kt < nkp; kt += P) {
+  for (int r = 0;; ++r) {
+    TileAt nxt;
+    const bool more = units.get(r + 1, nxt);
+    Addr an;
+    if (more) addr_of(nxt, an);
+    else an = ac;   // past the last tile: this tile's last step again (in bounds, unused)
 #pragma unroll
-    for (int u = 0; u < P; ++u) MOE_KSTEP_BODY(kt + u, u, (u + 1) % P);   // (u: macros use j, s)
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[0][j][v] = 0.0f;
+    for (int kt = 0; kt < nkp - P; kt += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) MOE_KSTEP_BODY(kt + u, u, (u + 1) % P, ac, kt + u + P);
+    }
+    // the last P steps request the next tile's first P steps (set u holds its step u)
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+      MOE_KSTEP_BODY(nkp - P + u, u, (u + 1) % P, an, more ? u : nk - 1);
+    // epilogue of this tile
+    if constexpr (PAIRED) {
+      // acc[0][0][r] (r < 8): gate row 8(r/4) + 4 fg + r%4 of the wave's 16, token fr;
+      // r + 8: the matching up row.  h -> bf16 into an LDS tile [32][64 + 8], then 16-byte
+      // row stores (one per thread).
+      constexpr int HLD = 72;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r0 = 4 * q + 2 * i;
+          float gv[2], uv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            gv[e] = acc[0][0][r0 + e];
+            uv[e] = acc[0][0][r0 + e + 8];
+            if constexpr (FP8) {
+              const int64_t hrow =
+                  (int64_t)cur.g * N + min(cur.ncol0 + 16 * w + 8 * q + 4 * fg + 2 * i + e, N - 1);
+              gv[e] *= a.sc0[hrow];
+              uv[e] *= a.sc1[hrow];
+            }
+          }
+          pk[i] = (uint32_t)f32_to_bf16(silu_fast(gv[0]) * uv[0]) |
+                  ((uint32_t)f32_to_bf16(silu_fast(gv[1]) * uv[1]) << 16);
+        }
+        *reinterpret_cast<uint2*>(Ht + fr * HLD + 16 * w + 8 * q + 4 * fg) =
+            make_uint2(pk[0], pk[1]);
+      }
+      __syncthreads();
+      bf16_t* Hout = (bf16_t*)a.out;
+      const int tid = threadIdx.x, row = tid >> 3, cc = (tid & 7) * 8;
+      const int m = cur.m0 + row, n = cur.ncol0 + cc;   // N % 64 == 0: n < N => n + 8 <= N
+      if (m < cur.M && n < N)
+        *reinterpret_cast<u32x4*>(Hout + (cur.row_begin + m) * N + n) =
+            *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
+      __syncthreads();   // the next tile's epilogue rewrites the transpose
+    } else {
+      int bcol[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bcol[nb] = GATED ? cur.ncol0 + 32 * w + fr : cur.ncol0 + 32 * NB * w + 32 * nb + fr;
+      float scl[NB];
+      load_scales<NB, GATED, FP8>(a, cur.g, bcol, scl);
+      store_tile<MB, NB, GATED, FP8>(acc, Ht, a.out, cur.row_begin, cur.M, cur.m0, cur.ncol0, N,
+                                     bcol, scl);
+    }
+    if (!more) break;
+    cur = nxt;
+    ac = an;
   }
-#undef MOE_KSTEP
+#undef MOE_KROT
 #undef MOE_KLOAD
 #undef MOE_KSTORE_B
 #undef MOE_KSTEP_BODY
-  __syncthreads();   // every wave is done with its LDS stages before the epilogue uses LDS
-  if constexpr (PAIRED) {
-    // acc[0][0][r] (r < 8): gate row 8(r/4) + 4 fg + r%4 of the wave's 16, token fr;
-    // r + 8: the matching up row.  h -> bf16 into an LDS tile [32][64 + 8], then 16-byte
-    // row stores (one per thread).
-    constexpr int HLD = 72;
-    bf16_t* Ht = smem;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      uint32_t pk[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r0 = 4 * q + 2 * i;
-        float gv[2], uv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          gv[e] = acc[0][0][r0 + e];
-          uv[e] = acc[0][0][r0 + e + 8];
-          if constexpr (FP8) {
-            const int64_t hrow = (int64_t)g * N + min(ncol0 + 16 * w + 8 * q + 4 * fg + 2 * i + e, N - 1);
-            gv[e] *= a.sc0[hrow];
-            uv[e] *= a.sc1[hrow];
-          }
-        }
-        pk[i] = (uint32_t)f32_to_bf16(silu_fast(gv[0]) * uv[0]) |
-                ((uint32_t)f32_to_bf16(silu_fast(gv[1]) * uv[1]) << 16);
-      }
-      *reinterpret_cast<uint2*>(Ht + fr * HLD + 16 * w + 8 * q + 4 * fg) = make_uint2(pk[0], pk[1]);
-    }
-    __syncthreads();
-    bf16_t* Hout = (bf16_t*)outp;
-    const int tid = threadIdx.x, row = tid >> 3, cc = (tid & 7) * 8;
-    const int m = m0 + row, n = ncol0 + cc;   // N % 64 == 0: n < N implies n + 8 <= N
-    if (m < M && n < N)
-      *reinterpret_cast<u32x4*>(Hout + (row_begin + m) * N + n) =
-          *reinterpret_cast<const u32x4*>(Ht + row * HLD + cc);
-    __syncthreads();   // the next tile's prologue overwrites the LDS
-  } else {
-    float scl[NB];
-    load_scales<NB, GATED, FP8>(a, g, bcol, scl);
-    store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
-  }
 }
 
 // One output tile over K steps [k0, k0 + nk) (callers pass the whole K), into outp.
@@ -824,6 +877,27 @@ __device__ inline int k_rotation(int g, int ncol0, int nk) {
   return (int)((cb + 13u * (unsigned)g) % (unsigned)nk);
 }
 
+// The tiles of a launch in which every group fits a skinny tile (at most 32 rows): the
+// block's units first, first + stride, ... of the static order, below total.
+template <bool GATED>
+struct StaticSkinnyTiles {
+  const GemmArgs* a;
+  const int* tiles;
+  int64_t first, stride, total;
+  __device__ bool get(int r, TileAt& t) const {
+    const int64_t tile = first + (int64_t)r * stride;
+    if (tile >= total) return false;
+    t.g = find_group(tiles, a->G, tile);
+    group_rows(*a, t.g, t.row_begin, t.M);
+    const int mt_g = (t.M + BM_SMALL - 1) / BM_SMALL;
+    const int local = (int)(tile - tiles[t.g]);       // ordered (n-tile, m-tile)
+    t.m0 = (local % mt_g) * BM_SMALL;
+    t.ncol0 = (local / mt_g) * tile_cols<GATED>(true, a->narrow_small);
+    t.rot = k_rotation<GATED>(t.g, t.ncol0, a->K / BK);
+    return true;
+  }
+};
+
 // One work unit: a tile of the table built in LDS.  Units from split0 on are the
 // launch's last tiles cut in two column halves (down GEMM only, see gemm_bf16_kernel):
 // unit split0 + 2 v + h is column half h of tile unit split0 + v.  Only 256- and 192-row
@@ -886,14 +960,11 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
                                             nk, rot, outp);
   else if (M - mt * BM_SMALL <= SKINNY_ROWS) {
     // (gate/up takes 64-column tiles only when every group fits a skinny tile)
+    const OneTile one{TileAt{g, M, mt * BM_SMALL, ncol0, rot, row_begin}};
     if (!narrow)
-      gemm_bf16_tile_skinny<2, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M,
-                                                            mt * BM_SMALL, ncol0, k0, nk, rot,
-                                                            outp);
+      gemm_skinny_stream<2, GATED, SKINNY_P, FP8>(a, smem, one);
     else
-      gemm_bf16_tile_skinny<1, GATED, skinny_p<FP8>(), FP8>(a, smem, g, row_begin, M,
-                                                            mt * BM_SMALL, ncol0, k0, nk, rot,
-                                                            outp);
+      gemm_skinny_stream<1, GATED, SKINNY_P, FP8>(a, smem, one);
   }
   else if (GATED || !narrow)
     gemm_bf16_tile_stream<2, GATED, STREAM_P2, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
@@ -936,7 +1007,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int x = blockIdx.x & 7;
   if (a.ctr == nullptr) {
     const int per = gridDim.x >> 3;
-    for (int64_t unit = (int64_t)x * per + (blockIdx.x >> 3); unit < total; unit += gridDim.x)
+    const int64_t first = (int64_t)x * per + (blockIdx.x >> 3);
+    if (a.skinny_all) {
+      // every tile is a skinny one: the block streams its units without draining
+      const StaticSkinnyTiles<GATED> units{&a, tiles, first, gridDim.x, total};
+      if (a.narrow_small)
+        gemm_skinny_stream<1, GATED, SKINNY_P, FP8>(a, smem, units);
+      else
+        gemm_skinny_stream<2, GATED, SKINNY_P, FP8>(a, smem, units);
+      return;
+    }
+    for (int64_t unit = first; unit < total; unit += gridDim.x)
       gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit, split0);
     return;
   }
@@ -1146,6 +1227,7 @@ hipError_t launch_gate_up(const moe_desc_t& d, const GemmRows& rows, const void*
   a.K = (int)d.d_model;
   a.n_tiles = (int)ceil_div(d.d_ff, 64);   // fp32 kernel: 64-column tiles
   a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
+  a.skinny_all = d.T <= SKINNY_ROWS && a.ctr == nullptr;   // a group holds at most T rows
   {
     // Every group fits a skinny tile (at most T rows each): take 64-column tiles when that
     // leaves less of the last round idle, e.g. 8 experts x 14336 columns give 896 tiles of
@@ -1180,6 +1262,7 @@ hipError_t launch_down(const moe_desc_t& d, const GemmRows& rows, const void* H,
     a.narrow_small = groups * ceil_div(d.d_model, 256) < 2 * (int64_t)device_cu_count();
   }
   a.ctr = dynamic_tiles(d, rows) ? ctr : nullptr;
+  a.skinny_all = d.T <= SKINNY_ROWS && a.ctr == nullptr;
   const int64_t mt = max_m_tiles(d, rows, BM_SMALL) * ceil_div(d.d_model, 128);
   if (!bf) return run_f32<false>(a, max_m_tiles(d, rows, 64), s);
   return ew.fp8 ? run_bf16<false, true>(a, mt, s) : run_bf16<false, false>(a, mt, s);
