@@ -42,7 +42,8 @@ def log(*a):
 
 
 # Layers timed beside the headline in the default run (one GPU, one after the other).
-SIDE_WORKLOADS = ("mixtral_decode", "fine_grained_shared", "switch_capacity")
+SIDE_WORKLOADS = ("mixtral_decode", "fine_grained_shared", "switch_capacity", "mixtral_decode_fp8",
+                  "switch_capacity_fp8")
 
 
 def main():

@@ -30,6 +30,9 @@ CASES = {
     "fine_shared_bias": gen.workload("fine_grained_shared").replace(T=300, d=192, E=40, F=128,
                                                                     weights="fp8"),
     "one_token": Workload("one_token", T=1, d=128, E=8, k=2, F=192, n_shared=1, weights="fp8"),
+    # 32 tokens, several streamed tiles per block in both GEMMs, shared expert
+    "stream_many_tiles": Workload("stream_many_tiles", T=32, d=1536, E=32, k=4, F=1536,
+                                  n_shared=1, bias_range=0.05, weights="fp8"),
 }
 
 

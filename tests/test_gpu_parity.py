@@ -62,6 +62,15 @@ CASES = {
                                   row_scales=tuple(np.linspace(2.0, 0.8, 8).round(4))),
     "capacity_above_decimal": Workload("capacity_above_decimal", T=400, d=64, E=8, k=2, F=64,
                                        capacity_factor=0.3),
+    # at most 32 tokens: every tile is a skinny one and each block streams several tiles
+    # back to back (the next tile's first K steps load under the current one's last), in
+    # both GEMMs: ~64 groups x 1024 columns; T sits at the 32-row limit
+    "stream_many_tiles": Workload("stream_many_tiles", T=32, d=1024, E=64, k=8, F=1024,
+                                  n_shared=1, bias_range=0.05),
+    # streamed 64-column tiles with drops and uneven, partly empty groups
+    "stream_capacity": Workload("stream_capacity", T=24, d=640, E=16, k=4, F=2048,
+                                capacity_factor=0.75,
+                                row_scales=tuple(np.linspace(2.2, 0.6, 16).round(4))),
     "f32_shared_capacity": Workload("f32_shared_capacity", T=130, d=64, E=12, k=3, F=128,
                                     n_shared=1, capacity_factor=1.0, dtype="f32", bias_range=0.02),
 }
@@ -206,7 +215,7 @@ def test_forward_is_deterministic(case):
 @pytest.mark.parametrize("name", ["fine_shared_bias", "ragged_wide_down", "prefill_skewed"])
 def test_batch_consistency(name):
     """Without a capacity, a token's output does not depend on the rest of the batch:
-    batch 1 and batch 64 give bit-identical rows ("Mixture-of-experts in practice",
+    batches of 1, 32 and 64 give bit-identical rows ("Mixture-of-experts in practice",
     inference-stability section, batch-consistency check).  The larger cases run the
     full batch with 256-row tiles, the dynamic tile order and the down GEMM's column
     halves, the sub-batches with 64-row and skinny tiles."""
@@ -214,7 +223,7 @@ def test_batch_consistency(name):
     inp = to_dev(gen.make_inputs(wl), DEV)
     args = (inp["router_bias"], inp["W_gate"], inp["W_up"], inp["W_down"], wl.k, 0.0)
     full, _, _ = moe.forward(inp["x"], inp["W_router"], *args)
-    for sub in ([7], list(range(64)), list(range(100, 300, 3))):
+    for sub in ([7], list(range(5, 37)), list(range(64)), list(range(100, 300, 3))):
         y, _, _ = moe.forward(inp["x"][sub].contiguous(), inp["W_router"], *args)
         assert torch.equal(y, full[sub])
 
