@@ -146,7 +146,7 @@ static moe_status_t experts_impl(const moe_desc_t* desc, const void* x, const in
   void* h = H ? H : w.H;
   MOE_HIP(launch_zero_i32(w.ctr, kTileCounters, s));
   MOE_HIP(launch_gate_up(d, token_choice_rows(d), x, perm_src, offsets, ew, h, w.ctr, s));
-  MOE_HIP(launch_down(d, token_choice_rows(d), h, offsets, ew, Yp, w.ctr + 8, s));
+  MOE_HIP(launch_down(d, token_choice_rows(d), h, offsets, ew, Yp, w.ctr + kTileCounters / 2, s));
   return MOE_OK;
 }
 
@@ -173,7 +173,7 @@ static moe_status_t gate_up_impl(const moe_desc_t* desc, const void* x, const in
   int32_t* ctr;
   if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (ctr) MOE_HIP(launch_zero_i32(ctr, 8, s));
+  if (ctr) MOE_HIP(launch_zero_i32(ctr, kTileCounters / 2, s));
   MOE_HIP(launch_gate_up(*desc, token_choice_rows(*desc), x, perm_src, offsets, ew, H, ctr, s));
   return MOE_OK;
 }
@@ -189,9 +189,9 @@ static moe_status_t down_impl(const moe_desc_t* desc, const void* H, const int32
   int32_t* ctr;
   if ((st = optional_ctr(*desc, workspace, workspace_bytes, &ctr)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (ctr) MOE_HIP(launch_zero_i32(ctr + 8, 8, s));
+  if (ctr) MOE_HIP(launch_zero_i32(ctr + kTileCounters / 2, kTileCounters / 2, s));
   MOE_HIP(launch_down(*desc, token_choice_rows(*desc), H, offsets, ew, Yp,
-                      ctr ? ctr + 8 : nullptr, s));
+                      ctr ? ctr + kTileCounters / 2 : nullptr, s));
   return MOE_OK;
 }
 
@@ -256,7 +256,7 @@ static moe_status_t forward_impl(const moe_desc_t* desc, const void* x, const vo
   }
   const GemmRows rows = token_choice_rows(d);
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + 8, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + kTileCounters / 2, s));
   MOE_HIP(launch_combine(d, w.Yp, w.slot_pos, w.topk_w, out, s));
   return MOE_OK;
 }
@@ -567,7 +567,7 @@ moe_status_t moe_forward_expert_choice(const moe_desc_t* desc, const void* x,
   MOE_HIP(launch_ec_select(w.probs, (int)d.T, E, (int)expert_choice_capacity(d), w.perm_src,
                            w.offsets, w.slot, f, s));
   MOE_HIP(launch_gate_up(d, rows, x, w.perm_src, w.offsets, ew, w.H, w.ctr, s));
-  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + 8, s));
+  MOE_HIP(launch_down(d, rows, w.H, w.offsets, ew, w.Yp, w.ctr + kTileCounters / 2, s));
   MOE_HIP(launch_ec_combine(d, rows.routed, w.Yp, w.slot, w.probs, out, s));
   return MOE_OK;
 }
