@@ -272,9 +272,8 @@ def run_workload(name, steps, warmup, dev):
                 "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = ("gemm_bf16_kernel<true, true> (gate/up + SiLU*mul, e4m3 weights)" if fp8
-                      else "gemm_bf16_kernel<true, false> (gate/up + SiLU*mul)" if wl.dtype == "bf16"
-                      else "gemm_f32_kernel<true>")
+    roof["kernel"] = gate_up_kernel(wl) + (" (gate/up + SiLU*mul, e4m3 weights)" if fp8
+                                           else " (gate/up + SiLU*mul)")
     roof["kernel_ms"] = stage_ms["gate_up"]
     roof["algorithmic_per_launch"] = flops_gate_up if bound != "hbm" else bytes_gate_up
 
@@ -360,8 +359,7 @@ def summarize_pmc(workload, fetch_csv, write_csv):
         return statistics.median([v for k in names for v in d[k]])
 
     import gen
-    gemm_name = "gemm_bf16_kernel<true, %s>" % ("true" if gen.workload(workload).weights == "fp8"
-                                                 else "false")
+    gemm_name = gate_up_kernel(gen.workload(workload))
     is_gemm = lambda k: gemm_name in k
     is_copy = lambda k: "MulFunctor" in k
     f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
@@ -378,6 +376,17 @@ def summarize_pmc(workload, fetch_csv, write_csv):
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def gate_up_kernel(wl):
+    """The kernel that runs the gate/up GEMM of workload wl: 8-bit weights and batches of
+    fewer than 65 tokens (no group can be large) take the 4-wave kernel, other bf16 layers
+    the 8-wave one; float32 layers the FMA kernel."""
+    if wl.dtype != "bf16":
+        return "gemm_f32_kernel<true>"
+    if wl.weights == "fp8":
+        return "gemm_bf16_kernel<true, true>"
+    return "gemm_w8_kernel<true>" if wl.T >= 65 else "gemm_bf16_kernel<true, false>"
 
 
 def host_info():
