@@ -379,14 +379,14 @@ def summarize_pmc(workload, fetch_csv, write_csv):
 
 
 def gate_up_kernel(wl):
-    """The kernel that runs the gate/up GEMM of workload wl: 8-bit weights and batches of
-    fewer than 65 tokens (no group can be large) take the 4-wave kernel, other bf16 layers
-    the 8-wave one; float32 layers the FMA kernel."""
+    """The kernel that runs the gate/up GEMM of workload wl: batches of fewer than 65 tokens
+    (no group can be large) take the 4-wave kernel, other bf16 layers the 8-wave one;
+    float32 layers the FMA kernel."""
     if wl.dtype != "bf16":
         return "gemm_f32_kernel<true>"
-    if wl.weights == "fp8":
-        return "gemm_bf16_kernel<true, true>"
-    return "gemm_w8_kernel<true>" if wl.T >= 65 else "gemm_bf16_kernel<true, false>"
+    fp8 = "true" if wl.weights == "fp8" else "false"
+    return (f"gemm_w8_kernel<true, {fp8}>" if wl.T >= 65
+            else f"gemm_bf16_kernel<true, {fp8}>")
 
 
 def host_info():

@@ -28,6 +28,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -1066,21 +1067,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 // 32 NB wn + 32 NB - 1 of the tile (NB = 1: a 128-column half, see gemm_w8_kernel).
 // The K steps, the k-slot permutation and the K rotation are those of the 4-wave tiles, so
 // every output element sums in the same order whichever kernel computes it.
-constexpr int W8_STAGE = 2 * BM_BIG * LDK;                        // bf16 per LDS stage
-constexpr size_t W8_LDS_BYTES = 2 * W8_STAGE * sizeof(bf16_t);    // 147456
+// 8-bit weights: the stage holds the weight rows as their e4m3 codes (64 bytes per row and
+// K step, 16-byte chunk c of row r at position c ^ ((r / 4) % 4)), widened to bf16 after the
+// fragment read; the per-row scales are applied to the sums in the epilogue.
+constexpr int W8_A_BYTES = BM_BIG * LDK * 2;                      // token rows of a stage
+constexpr int W8_STAGE_BF16 = 2 * W8_A_BYTES;                     // + 256 weight rows, bf16
+constexpr int W8_STAGE_FP8 = W8_A_BYTES + BM_BIG * BK;            // + 256 rows of codes
+constexpr size_t W8_LDS_BYTES = 2 * W8_STAGE_BF16;                // 147456
 
-template <int MH, int NB, bool GATED>
+template <int MH, int NB, bool GATED, bool FP8>
 __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
                                         int64_t row_begin, int M, int m0, int ncol0, int nk,
                                         int rot) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair the gate and up blocks in a wave");
-  constexpr int NBL = 2 * NB;              // weight rows loaded per thread and step / 64
+  constexpr int STAGE = FP8 ? W8_STAGE_FP8 : W8_STAGE_BF16;      // bytes
+  constexpr int NBL = FP8 ? NB : 2 * NB;   // 16-byte weight chunks per thread and step
   constexpr int NCH = MH + NBL;            // 16-byte chunks staged per thread and step
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
-  const int lr = tid >> 3, lc = (tid & 7) * 8;       // loads: rows lr + 64 i, k offset lc
+  const int lr = tid >> 3, lc = (tid & 7) * 8;       // token loads: rows lr + 64 i, k lc
   const int fr = lane & 31, fg = lane >> 5;
   const bf16_t* A = (const bf16_t*)a.A;
+  char* sm = (char*)smem;
   const int K = a.K, N = a.N;
 
   // Token rows (element offsets; the host bounds T*d and rows*F below 2^31).
@@ -1100,24 +1108,31 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
 #pragma unroll
     for (int i = 0; i < MH; ++i) aoff[i] = (base + aoff[i]) * K + lc;
   }
-  // Weight rows lr + 64 i of the tile: this expert's matrix (wave-uniform) + a 32-bit
-  // offset (N K < 2^31); gate/up: i = 0, 1 gate rows, i = 2, 3 the matching up rows.
-  const bf16_t* Bm[2] = {(const bf16_t*)a.B0 + (int64_t)g * N * K,
-                         (const bf16_t*)(GATED ? a.B1 : a.B0) + (int64_t)g * N * K};
-  int boff[NBL];
+  // Weight chunks: this expert's matrices (wave-uniform) + 32-bit byte offsets (N K < 2^31).
+  // bf16: chunk i is row lr + 64 i at k lc (gate/up: i = 0, 1 gate rows, 2, 3 the matching
+  // up rows); 8-bit: row tid / 4 + 128 i, 16-byte chunk tid % 4 (gate/up: i = 0 gate, 1 up).
+  typedef typename std::conditional<FP8, uint8_t, bf16_t>::type WT;
+  const WT* Bm[2] = {(const WT*)a.B0 + (int64_t)g * N * K,
+                     (const WT*)(GATED ? a.B1 : a.B0) + (int64_t)g * N * K};
+  int boff[NBL], bst[NBL];   // element offsets in the matrix, byte offsets in a stage
 #pragma unroll
   for (int i = 0; i < NBL; ++i) {
-    const int j = lr + 64 * i;
+    const int j = FP8 ? (tid >> 2) + 128 * i : lr + 64 * i;
     const int n = GATED ? ncol0 + (j & 127) : ncol0 + j;
-    boff[i] = min(n, N - 1) * K + lc;
+    boff[i] = min(n, N - 1) * K + (FP8 ? 16 * (tid & 3) : lc);
+    bst[i] = FP8 ? W8_A_BYTES + j * BK + 16 * ((tid & 3) ^ ((j >> 2) & 3))
+                 : W8_A_BYTES + (j * LDK + lc) * 2;
   }
-  // Fragment read offsets in a stage: token rows [0, 256), weight rows from 256.
+  // Fragment reads: token rows (bf16 offsets of row 32 MH wm + fr, lane half fg), weight
+  // rows (byte offsets of the nb-th 32-row block, row fr; 8-bit: per k16 step pair).
   const int ard = (32 * MH * wm + fr) * LDK + 32 * fg;
   int brd[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-    brd[nb] = (BM_BIG + (GATED ? 128 * nb + 32 * wn : 32 * NB * wn + 32 * nb) + fr) * LDK +
-              32 * fg;
+  for (int nb = 0; nb < 2; ++nb) {
+    const int R = (GATED ? 128 * nb + 32 * wn : 32 * NB * wn + 32 * nb) + fr;
+    brd[nb] = FP8 ? W8_A_BYTES + R * BK : W8_A_BYTES + (R * LDK + 32 * fg) * 2;
+  }
+  const int bx0 = 16 * ((2 * fg) ^ ((fr >> 2) & 3)), bx1 = 16 * ((2 * fg + 1) ^ ((fr >> 2) & 3));
 
   floatx16 acc[MH][NB];
 #pragma unroll
@@ -1133,24 +1148,32 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
 #define W8_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
 #define W8_LOAD_CHUNK(i, t)                                                                \
   {                                                                                        \
-    const int ko_ = W8_KSTEP(t) * BK;                                                      \
+    const int ks_ = W8_KSTEP(t);                                                           \
     if ((i) < MH)                                                                          \
-      st[i] = *reinterpret_cast<const u32x4*>(A + aoff[(i) < MH ? (i) : 0] + ko_);         \
+      st[i] = *reinterpret_cast<const u32x4*>(A + aoff[(i) < MH ? (i) : 0] + ks_ * BK);    \
     else                                                                                   \
-      st[i] = *reinterpret_cast<const u32x4*>(Bm[(i) >= MH + NB ? 1 : 0] +                 \
-                                              boff[(i) >= MH ? (i) - MH : 0] + ko_);       \
+      st[i] = *reinterpret_cast<const u32x4*>(                                             \
+          Bm[(i) >= MH + NBL / 2 ? 1 : 0] + boff[(i) >= MH ? (i) - MH : 0] + ks_ * BK);    \
   }
 #define W8_STORE_CHUNK(i, s)                                                               \
   {                                                                                        \
-    const int row_ = (i) < MH ? lr + 64 * (i) : BM_BIG + lr + 64 * ((i) - MH);             \
-    *reinterpret_cast<u32x4*>(smem + (s) * W8_STAGE + row_ * LDK + lc) = st[i];            \
+    const int o_ = (i) < MH ? ((lr + 64 * (i)) * LDK + lc) * 2 : bst[(i) >= MH ? (i) - MH : 0]; \
+    *reinterpret_cast<u32x4*>(sm + (s) * STAGE + o_) = st[i];                              \
   }
-#define W8_READ(af, bf, S, s)                                                              \
+#define W8_READ(af, bf, s0, s)                                                             \
   {                                                                                        \
+    const bf16_t* SA_ = (const bf16_t*)(sm + (s0) * STAGE);                                \
     _Pragma("unroll") for (int mb = 0; mb < MH; ++mb)                                      \
-      af[mb] = *reinterpret_cast<const bf16x8*>((S) + ard + mb * 32 * LDK + 8 * (s));      \
-    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                      \
-      bf[nb] = *reinterpret_cast<const bf16x8*>((S) + brd[nb] + 8 * (s));                  \
+      af[mb] = *reinterpret_cast<const bf16x8*>(SA_ + ard + mb * 32 * LDK + 8 * (s));      \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                    \
+      if constexpr (FP8) {                                                                 \
+        const uint2 q_ = *reinterpret_cast<const uint2*>(                                  \
+            sm + (s0) * STAGE + brd[nb] + ((s) >> 1 ? bx1 : bx0) + 8 * ((s) & 1));         \
+        bf[nb] = e4m3x8_to_bf16(q_.x, q_.y);                                               \
+      } else {                                                                             \
+        bf[nb] = *reinterpret_cast<const bf16x8*>(sm + (s0) * STAGE + brd[nb] + 16 * (s)); \
+      }                                                                                    \
+    }                                                                                      \
   }
 #define W8_MFMA(af, bf)                                                                    \
   _Pragma("unroll") for (int mb = 0; mb < MH; ++mb)                                        \
@@ -1171,12 +1194,11 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
     // stores chunks [NCH h / 2, NCH (h + 1) / 2) of step t+1 (loaded during step t-1) into
     // the other stage, last read during step t-1 by both groups; the compute phase runs the
     // MFMAs and reloads those chunks with step t+2.
-    const bf16_t* S = smem + (t & 1) * W8_STAGE;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 af[2][MH], bfr[2][NB];
-      W8_READ(af[0], bfr[0], S, 2 * h);
-      W8_READ(af[1], bfr[1], S, 2 * h + 1);
+      W8_READ(af[0], bfr[0], t & 1, 2 * h);
+      W8_READ(af[1], bfr[1], t & 1, 2 * h + 1);
 #pragma unroll
       for (int i = NCH * h / 2; i < NCH * (h + 1) / 2; ++i) W8_STORE_CHUNK(i, (t + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -1199,6 +1221,12 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
   if constexpr (GATED) {
     // h = SiLU(g) * u -> bf16 through an LDS tile [64 MH][128 + 8] (the stages are free:
     // the last phase ended with a barrier), then 16-byte row stores.
+    float sg = 1.0f, su = 1.0f;
+    if constexpr (FP8) {
+      const int n = min(ncol0 + 32 * wn + fr, N - 1);
+      sg = a.sc0[(int64_t)g * N + n];
+      su = a.sc1[(int64_t)g * N + n];
+    }
     constexpr int HLD = 136;
     bf16_t* Ht = smem;
 #pragma unroll
@@ -1206,7 +1234,9 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * MH * wm + 32 * mb + 8 * (r >> 2) + 4 * fg + (r & 3);
-        Ht[row * HLD + 32 * wn + fr] = f32_to_bf16(silu_fast(acc[mb][0][r]) * acc[mb][1][r]);
+        const float gv = FP8 ? acc[mb][0][r] * sg : acc[mb][0][r];
+        const float uv = FP8 ? acc[mb][1][r] * su : acc[mb][1][r];
+        Ht[row * HLD + 32 * wn + fr] = f32_to_bf16(silu_fast(gv) * uv);
       }
     __syncthreads();
     bf16_t* H = (bf16_t*)a.out;
@@ -1223,22 +1253,23 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
   } else {
     float* Y = (float*)a.out;
 #pragma unroll
-    for (int mb = 0; mb < MH; ++mb)
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = ncol0 + 32 * NB * wn + 32 * nb + fr;
+      const float sc = FP8 ? a.sc0[(int64_t)g * N + min(n, N - 1)] : 1.0f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int n = ncol0 + 32 * NB * wn + 32 * nb + fr;
+      for (int mb = 0; mb < MH; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 32 * MH * wm + 32 * mb + 8 * (r >> 2) + 4 * fg + (r & 3);
-          if (m < M && n < N) Y[(row_begin + m) * N + n] = acc[mb][nb][r];
+          if (m < M && n < N) Y[(row_begin + m) * N + n] = FP8 ? acc[mb][nb][r] * sc : acc[mb][nb][r];
         }
-      }
+    }
   }
 }
 
 // One work unit of the 8-wave kernel's table: a tile, or (down GEMM, units from split0
 // on) column half v & 1 of tile split0 + v / 2, with the whole tile's K rotation.
-template <bool GATED>
+template <bool GATED, bool FP8>
 __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const int* tiles,
                                         int64_t unit, int64_t split0, int nk) {
   constexpr int COLS = GATED ? 128 : 256;   // output columns per tile
@@ -1264,24 +1295,24 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
     if (half >= 0) {
       const int nc = ncol0 + 128 * half;
       if (nc >= a.N) return;   // a tile that holds no second half (N % 256 <= 128)
-      if (rows == 256) w8_tile<4, 1, false>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else if (rows == 192) w8_tile<3, 1, false>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else if (rows == 128) w8_tile<2, 1, false>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else w8_tile<1, 1, false>(a, smem, g, row_begin, M, m0, nc, nk, rot);
+      if (rows == 256) w8_tile<4, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
+      else if (rows == 192) w8_tile<3, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
+      else if (rows == 128) w8_tile<2, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
+      else w8_tile<1, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
       return;
     }
   }
-  if (rows == 256) w8_tile<4, 2, GATED>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else if (rows == 192) w8_tile<3, 2, GATED>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else if (rows == 128) w8_tile<2, 2, GATED>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else w8_tile<1, 2, GATED>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
+  if (rows == 256) w8_tile<4, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
+  else if (rows == 192) w8_tile<3, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
+  else if (rows == 128) w8_tile<2, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
+  else w8_tile<1, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
 }
 
 // Persistent 8-wave kernel over the tile table, in the order and XCD windows of
 // gemm_bf16_kernel (static, or claimed through the 8 per-XCD counters
 // a.ctr); the down GEMM with counters cuts a last round that is at most half full into
 // column halves, as there.
-template <bool GATED>
+template <bool GATED, bool FP8>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
@@ -1305,7 +1336,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
     const int per = gridDim.x >> 3;
     const int64_t first = (int64_t)x * per + (blockIdx.x >> 3);
     for (int64_t unit = first; unit < total; unit += gridDim.x)
-      w8_unit<GATED>(a, smem, tiles, unit, split0, nk);
+      w8_unit<GATED, FP8>(a, smem, tiles, unit, split0, nk);
     return;
   }
   for (;;) {
@@ -1324,7 +1355,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
     const int64_t unit = next_unit;
     __syncthreads();   // read by all before thread 0 writes the next one
     if (unit < 0) break;
-    w8_unit<GATED>(a, smem, tiles, unit, split0, nk);
+    w8_unit<GATED, FP8>(a, smem, tiles, unit, split0, nk);
   }
 }
 
@@ -1443,36 +1474,38 @@ static hipError_t allow_kernel_lds() {
   return hipSuccess;
 }
 
-template <bool GATED>
+template <bool GATED, bool FP8>
 static hipError_t allow_w8_lds() {
   static std::atomic<bool> done[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
-  e = hipFuncSetAttribute((const void*)gemm_w8_kernel<GATED>,
+  e = hipFuncSetAttribute((const void*)gemm_w8_kernel<GATED, FP8>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)W8_LDS_BYTES);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   return hipSuccess;
 }
 
-// bf16 weights with a batch in which some group may be large (a group holds at most T
+// bf16 layers with a batch in which some group may be large (a group holds at most T
 // rows): the whole GEMM runs in the 8-wave kernel (small groups as 64-row tiles there; on
 // the Switch-shaped layer this beats sending them to gemm_bf16_kernel's streaming tiles in
-// a second launch: gate/up 1.05 -> 1.01 ms, down 0.61 -> 0.52 ms).  Decode-sized batches and
-// 8-bit weights stay with gemm_bf16_kernel.  Returns whether it launched.
+// a second launch: gate/up 1.05 -> 1.01 ms, down 0.61 -> 0.52 ms).  Decode-sized batches
+// stay with gemm_bf16_kernel.  Returns whether it launched.
 template <bool GATED>
 static hipError_t run_w8(const GemmArgs& a, const moe_desc_t& d, bool fp8, hipStream_t s,
                          bool* launched) {
   *launched = false;
-  if (d.dtype != MOE_DTYPE_BF16 || fp8 ||
-      d.T < (GATED ? SMALL_GROUP_ROWS_GATED : SMALL_GROUP_ROWS_DOWN))
+  if (d.dtype != MOE_DTYPE_BF16 || d.T < (GATED ? SMALL_GROUP_ROWS_GATED : SMALL_GROUP_ROWS_DOWN))
     return hipSuccess;
-  hipError_t e = allow_w8_lds<GATED>();
+  hipError_t e = fp8 ? allow_w8_lds<GATED, true>() : allow_w8_lds<GATED, false>();
   if (e != hipSuccess) return e;
   const int64_t grid = round_up(device_cu_count(), 8);
-  hipLaunchKernelGGL(gemm_w8_kernel<GATED>, dim3((unsigned)grid), dim3(512), W8_LDS_BYTES, s, a);
+  if (fp8)
+    hipLaunchKernelGGL((gemm_w8_kernel<GATED, true>), dim3((unsigned)grid), dim3(512), W8_LDS_BYTES, s, a);
+  else
+    hipLaunchKernelGGL((gemm_w8_kernel<GATED, false>), dim3((unsigned)grid), dim3(512), W8_LDS_BYTES, s, a);
   e = hipGetLastError();
   *launched = e == hipSuccess;
   return e;
