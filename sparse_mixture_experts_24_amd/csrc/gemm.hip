@@ -874,11 +874,17 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, 
 // their weight streams spread over the HBM channels instead of all reading the same column
 // range of rows at a common stride.  A function of the expert and the output columns only
 // (in units of the large tiles' width, whatever the tile kind), so the summation order of
-// an output element does not depend on the rest of the batch.
+// an output element does not depend on the rest of the batch.  Blocks of W8_NBLOCK
+// consecutive large-tile column blocks share a start: the 8-wave kernel runs such a block's
+// n-tiles of the same m-tiles together (8 m-tiles x 4 n-tiles per XCD window), and with a
+// common K position they read each token-row chunk from L2 once for the block (prefill
+// 2.86 -> 2.83 ms, fine-grained 7.46 -> 7.34 ms, Switch 1.75 -> 1.73 ms, decode 0.484 ->
+// 0.480 ms against a start per column block).
+constexpr int W8_NBLOCK = 4;
 template <bool GATED>
 __device__ inline int k_rotation(int g, int ncol0, int nk) {
   const unsigned cb = (unsigned)ncol0 / (GATED ? 128u : 256u);
-  return (int)((cb + 13u * (unsigned)g) % (unsigned)nk);
+  return (int)((cb / W8_NBLOCK + 13u * (unsigned)g) % (unsigned)nk);
 }
 
 // The tiles of a launch in which every group fits a skinny tile (at most 32 rows): the
@@ -1285,9 +1291,22 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
   group_rows(a, g, row_begin, M);
   const int bm = small_group<GATED>(M) ? BM_SMALL : BM_BIG;
   const int mt_g = (M + bm - 1) / bm;
-  const int local = (int)(unit - tiles[g]);   // ordered (n-tile, m-tile)
-  const int mt = local % mt_g;
-  const int ncol0 = (local / mt_g) * COLS;
+  // A group's tiles in blocks of W8_NBLOCK n-tiles (the last block may be narrower); within
+  // a block m-tile major, so a window of 32 consecutive units is 8 m-tiles x 4 n-tiles
+  // sharing their K positions.
+  const int local = (int)(unit - tiles[g]);
+  const int NT = (a.N + COLS - 1) / COLS, full = NT / W8_NBLOCK;
+  int mt, nt;
+  if (local < full * mt_g * W8_NBLOCK) {
+    const int nb = local / (mt_g * W8_NBLOCK), rem = local % (mt_g * W8_NBLOCK);
+    mt = rem / W8_NBLOCK;
+    nt = nb * W8_NBLOCK + rem % W8_NBLOCK;
+  } else {
+    const int rem = local - full * mt_g * W8_NBLOCK, wd = NT - full * W8_NBLOCK;
+    mt = rem / wd;
+    nt = full * W8_NBLOCK + rem % wd;
+  }
+  const int ncol0 = nt * COLS;
   const int rows = m_tile_rows<GATED>(M, mt);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
   const int m0 = mt * bm;
