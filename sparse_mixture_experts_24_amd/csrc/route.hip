@@ -8,10 +8,10 @@
 //
 // bf16 layers: the logits GEMM runs on MFMA (v_mfma_f32_16x16x32_bf16, fp32
 // accumulation).  One block = 4 wave64s over BT tokens.  EW waves split the experts
-// into slabs of 16*EPW; KS = 4/EW waves split the reduction over d.  Each lane reads
-// 32 contiguous bytes of a row per 64-wide k chunk (a row's 128 bytes come from 4
-// lanes), and the two MFMAs of the chunk take the first and second 16 bytes: A and B
-// use the same k mapping, so the sum is over the same pairs as a plain dot product.
+// into slabs of 16*EPW; KS = 4/EW waves split the reduction over d.  A wave's rows of a
+// 64-wide k chunk are loaded 8 lanes per 128-byte row segment and put into MFMA operand
+// order through a wave-private LDS buffer; lane group g of MFMA half h takes the 8 k values
+// at 16 g + 8 h for A and B alike, so the sum is over the same pairs as a plain dot product.
 // The top-k runs one wavefront per token; its reductions move data between lanes with DPP
 // and v_permlane16/32_swap (no LDS round trips).
 #include <math.h>
@@ -22,6 +22,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Lane exchanges for wave-wide reductions.  Inside a 16-lane row: DPP quad swaps (1,0,3,2)
 // and (2,3,0,1), then the half-row and row mirrors; across rows: v_permlane16_swap and
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   __shared__ float lg[KS][BT][E_PAD];
   __shared__ float pw[4][E_PAD];
   __shared__ int cnt[E_PAD];
+  __shared__ __align__(16) unsigned char rbuf[4 * 16 * (TPW + EPW) * 128];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ew = w / KS, ks = w % KS;
@@ -416,26 +418,41 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   const int r = lane & 15, g = lane >> 4;
   for (int e = threadIdx.x; e < E_PAD; e += blockDim.x) cnt[e] = 0;
 
-  const bf16_t* arow[TPW];
+  // Row segments: 16 bytes per lane, 8 lanes per 128-byte row segment of a 64-wide k chunk
+  // (the loads coalesce; a lane per row, as the MFMA operand layout has it, runs the load
+  // path at a quarter of its rate).  Segment i of the lane: token row 8 i + lane / 8 of the
+  // block (i < 2 TPW), then expert row 8 (i - 2 TPW) + lane / 8 of the wave's slab, chunk
+  // lane % 8.  Expert rows past E (padding of the last slab) read row E-1 and token rows
+  // past T read row T-1; their logits are never used.  32-bit element offsets: T d and E d
+  // are below 2^31.
+  constexpr int NSEG = 2 * (TPW + EPW);
+  int soff[NSEG];
 #pragma unroll
-  for (int tb = 0; tb < TPW; ++tb) {
-    const int t = min(t0 + tb * 16 + r, T - 1);
-    arow[tb] = x + (size_t)t * d + g * 16;
+  for (int i = 0; i < NSEG; ++i) {
+    const int rr = 8 * (i < 2 * TPW ? i : i - 2 * TPW) + (lane >> 3);
+    const int row = i < 2 * TPW ? min(t0 + rr, T - 1) : min(ew * EPW * 16 + rr, E - 1);
+    soff[i] = row * d + 8 * (lane & 7);
   }
-  // Expert rows past E (padding of the last slab) read row E-1; their logits are never used.
-  const bf16_t* brow[EPW];
+  // The wave's LDS buffer of one chunk: its 16 TPW token rows, then its 16 EPW expert rows,
+  // 128 bytes each, 16-byte chunk c of row r at position c ^ ((r / 2) % 8) (conflict-free
+  // stores and fragment reads).  Written and read by this wave only, in program order, so no
+  // barrier.  Fragment (row r, k16 half h) of lane group g: chunk 2 g + h.
+  unsigned char* wbuf = rbuf + w * (16 * (TPW + EPW) * 128);
+  int swr[NSEG], frd[2];
 #pragma unroll
-  for (int eb = 0; eb < EPW; ++eb) {
-    const int e = (ew * EPW + eb) * 16 + r;
-    brow[eb] = Wr + (size_t)min(e, E - 1) * d + g * 16;
+  for (int i = 0; i < NSEG; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    swr[i] = row * 128 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
   }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) frd[h] = r * 128 + 16 * ((2 * g + h) ^ ((r >> 1) & 7));
   floatx4 acc[TPW][EPW];
 #pragma unroll
   for (int tb = 0; tb < TPW; ++tb)
 #pragma unroll
     for (int eb = 0; eb < EPW; ++eb) acc[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // This wave's 64-wide k chunks are c = ks + KS*j, j < nj.  Their fragments go through a
+  // This wave's 64-wide k chunks are c = ks + KS*j, j < nj.  Their row segments go through a
   // ring of R register slots, loaded R-1 chunks ahead of the MFMAs.  Whole passes over
   // the ring run unguarded (a load past the end reads the last chunk again, a valid
   // address, and is never used); the remaining chunks, already loaded, finish after the
@@ -443,27 +460,29 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   // R-1 chunks stay in flight while a chunk's MFMAs run.
   const int nchunk = d / 64;
   const int nj = (nchunk - ks + KS - 1) / KS;
-  bf16x8 xa[R][TPW][2], xb[R][EPW][2];
+  u32x4 seg[R][NSEG];
 #define R_LOAD(SLOT, j)                                                                     \
   {                                                                                         \
     const int c_ = ks + KS * min((j), nj - 1);                                              \
-    _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb) {                                    \
-      const bf16x8* pa = reinterpret_cast<const bf16x8*>(arow[tb] + c_ * 64);               \
-      xa[SLOT][tb][0] = pa[0];                                                              \
-      xa[SLOT][tb][1] = pa[1];                                                              \
-    }                                                                                       \
-    _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb) {                                    \
-      const bf16x8* pb = reinterpret_cast<const bf16x8*>(brow[eb] + c_ * 64);               \
-      xb[SLOT][eb][0] = pb[0];                                                              \
-      xb[SLOT][eb][1] = pb[1];                                                              \
-    }                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < NSEG; ++i)                                        \
+      seg[SLOT][i] = *reinterpret_cast<const u32x4*>((i < 2 * TPW ? x : Wr) + soff[i] + c_ * 64); \
   }
 #define R_MFMA(SLOT)                                                                        \
-  _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                        \
-    _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                      \
-      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                         \
-        acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
-            xa[SLOT][tb][h], xb[SLOT][eb][h], acc[tb][eb], 0, 0, 0);
+  {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < NSEG; ++i)                                        \
+      *reinterpret_cast<u32x4*>(wbuf + swr[i]) = seg[SLOT][i];                              \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                         \
+      bf16x8 fa_[TPW], fb_[EPW];                                                            \
+      _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                    \
+        fa_[tb] = *reinterpret_cast<const bf16x8*>(wbuf + tb * 16 * 128 + frd[h]);          \
+      _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                    \
+        fb_[eb] = *reinterpret_cast<const bf16x8*>(wbuf + (TPW + eb) * 16 * 128 + frd[h]);  \
+      _Pragma("unroll") for (int tb = 0; tb < TPW; ++tb)                                    \
+        _Pragma("unroll") for (int eb = 0; eb < EPW; ++eb)                                  \
+          acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa_[tb], fb_[eb], acc[tb][eb], \
+                                                                0, 0, 0);                   \
+    }                                                                                       \
+  }
   if (nj > 0) {
 #pragma unroll
     for (int q = 0; q < R - 1; ++q) R_LOAD(q, q);
