@@ -11,12 +11,12 @@
 // the device from the dispatch offsets, so skewed per-expert counts need no host round
 // trip; tiles are ordered (group, n-tile, m-tile) and dealt to the XCDs in windows of
 // consecutive tiles, so the m-tiles that share a weight tile run on the same L2:
-//   * gemm_w8_kernel (bf16 weights, batches in which a group can be large): 8 waves in
+//   * gemm_w8_kernel (batches in which a group can be large; bf16 or 8-bit weights): 8 waves in
 //     ping-pong pairs per SIMD, 64..256-row x 256-weight-row tiles, token rows and weights
 //     both staged through LDS;
-//   * gemm_bf16_kernel (decode-sized batches and 8-bit weights): 4 waves, 256-row tiles
-//     with the weights loaded straight into MFMA operand registers, 64-row streaming tiles
-//     and barrier-free skinny tiles for groups of at most 32 rows;
+//   * gemm_bf16_kernel (batches in which no group can be large: fewer tokens than the
+//     small-group bound): 4 waves, 64-row streaming tiles and barrier-free skinny tiles
+//     for groups of at most 32 rows;
 //   * v_mfma_f32_32x32x16_bf16 accumulators; for the gate/up GEMM a wave holds the gate
 //     and up blocks of the same columns, so SiLU(g)*u is formed in registers and H is
 //     stored once, in bf16;
@@ -66,22 +66,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
-
-// Weight registers of one K step: bf16 [nb][k16 step] operands, or the 32 code bytes of
-// each lane for 8-bit weights (k16 step s in bytes [8s, 8s + 8)).
-template <bool FP8, int NB>
-struct BRegs {
-  bf16x8 v[NB][4];
-  __device__ __forceinline__ bf16x8 op(int nb, int s) const { return v[nb][s]; }
-};
-template <int NB>
-struct BRegs<true, NB> {
-  u32x4 v[NB][2];
-  __device__ __forceinline__ bf16x8 op(int nb, int s) const {
-    const u32x4 q = v[nb][s >> 1];
-    return (s & 1) ? e4m3x8_to_bf16(q[2], q[3]) : e4m3x8_to_bf16(q[0], q[1]);
-  }
-};
 
 // Geometry of group g.
 __device__ inline void group_rows(const GemmArgs& a, int g, int64_t& row_begin, int& M) {
@@ -146,32 +130,23 @@ __device__ inline float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// ------------------------------------------------------------------ bf16 MFMA kernel
-// Output tile BM x BN, BN = 256 (gate/up: 128 gate + the matching 128 up columns).
-// BM = 32*MB rows: 256 for groups that are not small (small_group below; the last tile
-// of a group 64, 128, 192 or 256 rows, to fit the remainder), 64 for small ones, so small
-// experts (decode, the tail of skewed or capacity-limited routing) do not pay for 256-row
-// MFMA tiles.  Wave w owns B rows [64w, 64w + 64) of the tile (gate/up: 32 gate + 32 up)
-// and all BM A rows: MB x 2 blocks of 32x32 accumulators.
-//   * B (the weights) goes straight from global memory into MFMA operand registers,
-//     three register sets deep: the set for K-step t+2 is issued at step t, so a weight
-//     load has two steps of work to arrive;
-//   * A (the token rows) is staged once per block through LDS (two stages, rows padded to
-//     72 bf16 so fragment reads hit distinct banks) and read by all four waves;
-//   * inside a 64-wide K step the MFMA k-slots are permuted: step s, lane half g uses the
-//     physical columns [32g + 8s, 32g + 8s + 8), for A and B alike, so each lane's B data
-//     for the whole step is 64 contiguous bytes of one weight row;
-//   * each K step is one scheduling region in which the fragment reads of k16 step s+1
-//     and the global loads are interleaved with the MFMAs of step s.
+// ------------------------------------------------------------------ bf16 MFMA tiles
+// Output tiles of 64 to 256 rows (256-row tiles for large groups, with the remainder in one
+// tile of 64, 128, 192 or 256 rows; 64-row tiles for small groups, so small experts do not
+// pay for 256-row MFMA tiles) by 128 h columns (gate/up: the gate rows of those columns
+// and the matching up rows) or 256 output columns (down).
+//   * K is walked in 64-wide steps; inside a step the MFMA k-slots are permuted: k16 step s,
+//     lane half g uses the physical columns [32g + 8s, 32g + 8s + 8), for A and B alike;
+//   * token rows are staged through LDS rows padded to 72 bf16 (LDK), so the fragment
+//     reads of a wavefront hit distinct banks.
 constexpr int BK = 64, LDK = BK + 8;
 constexpr int BM_BIG = 256, BM_SMALL = 64;
-// Row counts from which a group takes the MFMA tiles instead of 64-row tiles.  gate/up: a
-// group of 65-128 rows runs faster as one 128-row tile (its weights read once) than as
-// two 64-row streaming tiles; the down GEMM's 64-row tiles, 256 columns wide, stay ahead
-// up to 80 rows.  (Measured on the Switch-shaped layer, whose groups hold 32-320 rows:
+// Row counts from which a group takes 256-row tiles (and a 64- to 256-row remainder)
+// instead of 64-row tiles.  gate/up: a group of 65-128 rows runs faster as one 128-row tile
+// (its weights read once) than as two 64-row tiles; the down GEMM's 64-row tiles, 256
+// columns wide, stay ahead up to 80 rows.  (Measured on the Switch-shaped layer, whose groups hold 32-320 rows:
 // gate/up 1.13 -> 1.07 ms, down 0.59 -> 0.56 ms against one bound of 128 rows for both.)
 constexpr int SMALL_GROUP_ROWS_GATED = 65, SMALL_GROUP_ROWS_DOWN = 81;
-constexpr size_t GEMM_LDS_BYTES = 2 * BM_BIG * LDK * sizeof(bf16_t);   // 73728
 
 // Tile shape of a group with M rows: 256-row tiles for large groups, 64-row tiles for
 // small ones.  Columns per tile: gate/up 128 (each wave one 32-column block of gate and
@@ -262,9 +237,8 @@ __device__ __forceinline__ void load_scales(const GemmArgs& a, int g, const int 
 }
 
 // A 64-row tile whose work is streaming its weights (small groups: decode, the tail of
-// skewed or capacity-limited routing).  Same math as gemm_bf16_tile<2, NB, GATED>, but the
-// weights are read with whole 128-byte row segments per 8 lanes (HBM-friendly, where the
-// register-direct layout has 32 rows x 32 bytes per load) and put into MFMA order through
+// skewed or capacity-limited routing).  The weights are read with whole 128-byte row
+// segments per 8 lanes (the loads coalesce into full HBM bursts) and put into MFMA order through
 // a wave-private LDS buffer: two stages of [NB*32 rows][64 bf16], 16-byte chunks XOR
 // swizzled (chunk c of row r at c ^ ((r/2)%8)) so both the stores and the fragment reads
 // are conflict-free.  P steps of weights are in flight per wave (P register sets).
@@ -281,8 +255,7 @@ constexpr int STREAM_P2 = 2, STREAM_P1 = 8;
 // 0.309 ms and the 8-bit one from 0.217 to 0.194 ms; 6 or 8 steps are no faster.)
 constexpr int SKINNY_ROWS = 32;
 constexpr int SKINNY_P = 4;
-constexpr size_t KERNEL_LDS_BYTES =
-    GEMM_LDS_BYTES > SMALL_LDS_BYTES ? GEMM_LDS_BYTES : SMALL_LDS_BYTES;
+constexpr size_t KERNEL_LDS_BYTES = SMALL_LDS_BYTES;
 // 8-bit weights: a K step of a row is 64 bytes, read by 4 lanes (16 rows per load); the
 // wave-private stage holds [NB*32 rows][64 bytes], 16-byte chunk c of row r at position
 // c ^ ((r/4)%4), and a fragment is one 8-byte read, converted to bf16 after the read.
@@ -649,227 +622,6 @@ __device__ __forceinline__ void gemm_skinny_stream(const GemmArgs& a, bf16_t* sm
 #undef MOE_KSTEP_BODY
 }
 
-// One output tile over K steps [k0, k0 + nk) (callers pass the whole K), into outp.
-template <int MB, int NB, bool GATED, bool FP8>
-__device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& a, bf16_t* smem, int g,
-                                               int64_t row_begin, int M, int m0, int ncol0,
-                                               int k0, int nk, int rot, void* outp) {
-  static_assert(!GATED || NB == 2, "gate/up tiles pair one gate and one up block per wave");
-  constexpr int BMT = 32 * MB;
-  constexpr int STAGE = BMT * LDK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = tid >> 3, lc = (tid & 7) * 8;       // A load: row lr + 32i, k offset lc
-  const int fr = lane & 31, fg = lane >> 5;          // fragment row / lane half
-  const bf16_t* A = (const bf16_t*)a.A + k0 * BK;
-  const int K = a.K, N = a.N;
-
-  // A: element offsets (32-bit; the host bounds T*d and rows*F below 2^31).  The
-  // perm_src gathers of the routed rows are issued together, then converted.
-  int aoff[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + lr + 32 * i;
-    aoff[i] = m < M ? m : 0;
-  }
-  if (GATED && g < a.E) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) aoff[i] = a.perm_src[row_begin + aoff[i]];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) aoff[i] = aoff[i] / a.topk * K + lc;
-  } else {
-    const int base = GATED ? 0 : (int)row_begin;     // shared expert: token m; down: row
-#pragma unroll
-    for (int i = 0; i < MB; ++i) aoff[i] = (base + aoff[i]) * K + lc;
-  }
-  // B: this lane's NB weight rows (one per n-block), 32 contiguous k per lane half
-  // (64 bytes of bf16, or 32 bytes of 8-bit codes)
-  constexpr int WB = FP8 ? 1 : 2;                    // bytes per weight
-  const char* pb[NB];
-  int bcol[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = GATED ? ncol0 + 32 * w + fr : ncol0 + 32 * NB * w + 32 * nb + fr;
-    const char* base = (const char*)((GATED && nb == 1) ? a.B1 : a.B0);
-    bcol[nb] = n;
-    pb[nb] = base + (((int64_t)g * N + min(n, N - 1)) * K + 32 * fg + k0 * BK) * WB;
-  }
-
-  floatx16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  BRegs<FP8, NB> b0, b1, b2;   // three B register sets
-  u32x4 ra[MB];
-
-  // Step t reads K step (t + rot) mod nk (see k_rotation).
-#define MOE_KSTEP(t) ((min((t), nk - 1) + rot) - ((min((t), nk - 1) + rot) >= nk ? nk : 0))
-#define MOE_LOAD_B(set, t)                                                                 \
-  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                      \
-    if constexpr (FP8) {                                                                   \
-      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                        \
-        set.v[nb][h] = *reinterpret_cast<const u32x4*>(pb[nb] + MOE_KSTEP(t) * BK + 16 * h); \
-    } else {                                                                               \
-      _Pragma("unroll") for (int s = 0; s < 4; ++s)                                        \
-        set.v[nb][s] =                                                                     \
-            *reinterpret_cast<const bf16x8*>(pb[nb] + MOE_KSTEP(t) * BK * 2 + 16 * s);     \
-    }                                                                                      \
-  }
-#define MOE_LOAD_A(t)                                                                      \
-  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                           \
-    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + MOE_KSTEP(t) * BK);
-#define MOE_STORE_A(st)                                                                    \
-  {                                                                                        \
-    bf16_t* As_ = smem + (st) * STAGE;                                                     \
-    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                         \
-      *reinterpret_cast<u32x4*>(As_ + (lr + 32 * i) * LDK + lc) = ra[i];                   \
-  }
-#define MOE_READ_A(af, st, s)                                                              \
-  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
-    af[mb] = *reinterpret_cast<const bf16x8*>(smem + (st) * STAGE + (mb * 32 + fr) * LDK + \
-                                              32 * fg + 8 * (s));
-#define MOE_MFMA(af, set, s)                                                               \
-  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                        \
-    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                      \
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], set.op(nb, s),          \
-                                                            acc[mb][nb], 0, 0, 0);
-#define MOE_COMPUTE(set, st)                                                               \
-  {                                                                                        \
-    bf16x8 fa[MB], fb[MB];                                                                 \
-    MOE_READ_A(fa, st, 0);                                                                 \
-    MOE_READ_A(fb, st, 1);                                                                 \
-    MOE_MFMA(fa, set, 0);                                                                  \
-    MOE_READ_A(fa, st, 2);                                                                 \
-    MOE_MFMA(fb, set, 1);                                                                  \
-    MOE_READ_A(fb, st, 3);                                                                 \
-    MOE_MFMA(fa, set, 2);                                                                  \
-    MOE_MFMA(fb, set, 3);                                                                  \
-  }
-  // Region order: the 2*MB fragment reads of k16 steps 0 and 1, then per k16 step s a
-  // quarter of the MB + 4*NB global loads and MB x {NB MFMAs, (read for step s+2)}.
-#define MOE_INTERLEAVE(s, reads)                                                           \
-  {                                                                                        \
-    constexpr int NGL_ = MB + 4 * NB;                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x020, NGL_ * ((s) + 1) / 4 - NGL_ * (s) / 4, 0); \
-    _Pragma("unroll") for (int j_ = 0; j_ < MB; ++j_) {                                    \
-      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);                                  \
-      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        \
-    }                                                                                      \
-  }
-  // Steps t >= nk (padding the step count up to a multiple of 3) read zero A rows, so the
-  // accumulators are unchanged, and the loop body has no exits.
-#define MOE_STEP_END(t, cur, nxt2)                                                             \
-  {                                                                                        \
-    MOE_LOAD_A(min((t) + 1, nk - 1));                                                      \
-    MOE_LOAD_B(nxt2, (t) + 2);                                                             \
-    MOE_COMPUTE(cur, (t) & 1);                                                             \
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);                                \
-    MOE_INTERLEAVE(0, 1)                                                                   \
-    MOE_INTERLEAVE(1, 1)                                                                   \
-    MOE_INTERLEAVE(2, 0)                                                                   \
-    MOE_INTERLEAVE(3, 0)                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    if ((t) + 1 >= nk) {                                                                   \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) ra[i] = u32x4{0u, 0u, 0u, 0u};        \
-    }                                                                                      \
-    MOE_STORE_A(((t) + 1) & 1);                                                            \
-    __syncthreads();                                                                       \
-  }
-
-  // Scheduling of a k16 step of the first half: a quarter of the weight loads, then MB x
-  // {NB MFMAs, one fragment read for the second half}.
-#define MOE_SGB_HALF                                                                       \
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * NB, 0);                                  \
-  _Pragma("unroll") for (int j_ = 0; j_ < MB; ++j_) {                                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);                                    \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
-  }
-  // K step t (rows in stage t & 1, weights in set cur; the registers ra hold the rows of
-  // step t+1, requested halfway through step t-1).  Halfway through the step, after the
-  // MFMAs of k16 steps 0 and 1, ra goes to the other stage (read last during step t-1,
-  // before the barrier that ended it) and is refilled with the rows of step t+2, so the
-  // LDS writes overlap the MFMAs of k16 steps 2 and 3 instead of stalling the step's end.
-#define MOE_STEP(t, cur, nxt2)                                                             \
-  {                                                                                        \
-    MOE_LOAD_B(nxt2, (t) + 2);                                                             \
-    {                                                                                      \
-      bf16x8 fa[MB], fb[MB];                                                               \
-      MOE_READ_A(fa, (t) & 1, 0);                                                          \
-      MOE_READ_A(fb, (t) & 1, 1);                                                          \
-      MOE_MFMA(fa, cur, 0);                                                                \
-      MOE_READ_A(fa, (t) & 1, 2);                                                          \
-      MOE_MFMA(fb, cur, 1);                                                                \
-      MOE_READ_A(fb, (t) & 1, 3);                                                          \
-      MOE_STORE_A(((t) + 1) & 1);                                                          \
-      MOE_LOAD_A(min((t) + 2, nk - 1));                                                    \
-      MOE_MFMA(fa, cur, 2);                                                                \
-      MOE_MFMA(fb, cur, 3);                                                                \
-    }                                                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);                                \
-    MOE_SGB_HALF                                                                           \
-    MOE_SGB_HALF                                                                           \
-    __builtin_amdgcn_sched_group_barrier(0x200, MB, 0);                                    \
-    __builtin_amdgcn_sched_group_barrier(0x020, MB / 2, 0);                                \
-    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);                               \
-    __builtin_amdgcn_sched_group_barrier(0x020, MB - MB / 2, 0);                           \
-    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    __syncthreads();                                                                       \
-  }
-
-  // Gate/up 256-row tiles store their next rows halfway through each step; the other tiles
-  // (down, and the 128/64-row remainders) store them at the end of the step: the mid-step
-  // order needs more registers live across the step and spills there.
-  if constexpr (GATED && MB == 8) {
-  MOE_LOAD_B(b0, 0);
-  MOE_LOAD_B(b1, 1);
-  MOE_LOAD_A(0);
-  MOE_STORE_A(0);
-  MOE_LOAD_A(min(1, nk - 1));
-  __syncthreads();
-  // Whole triples of steps (the B register sets rotate with period 3), then the last
-  // nk % 3 steps; loads past the last step are clamped to it (in bounds, never used).
-  int kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    MOE_STEP(kt, b0, b2);
-    MOE_STEP(kt + 1, b1, b0);
-    MOE_STEP(kt + 2, b2, b1);
-  }
-  if (kt < nk) MOE_STEP(kt, b0, b2);
-  if (kt + 1 < nk) MOE_STEP(kt + 1, b1, b0);
-  } else {
-  MOE_LOAD_B(b0, 0);
-  MOE_LOAD_B(b1, 1);
-  MOE_LOAD_A(0);
-  MOE_STORE_A(0);
-  __syncthreads();
-  const int nk3 = (nk + 2) / 3 * 3;
-  for (int kt = 0; kt < nk3; kt += 3) {
-    MOE_STEP_END(kt, b0, b2);
-    MOE_STEP_END(kt + 1, b1, b0);
-    MOE_STEP_END(kt + 2, b2, b1);
-  }
-  }
-#undef MOE_KSTEP
-#undef MOE_LOAD_B
-#undef MOE_LOAD_A
-#undef MOE_STORE_A
-#undef MOE_READ_A
-#undef MOE_MFMA
-#undef MOE_SGB_HALF
-#undef MOE_STEP
-#undef MOE_COMPUTE
-#undef MOE_INTERLEAVE
-#undef MOE_STEP_END
-
-  float scl[NB];
-  load_scales<NB, GATED, FP8>(a, g, bcol, scl);
-  store_tile<MB, NB, GATED, FP8>(acc, smem, outp, row_begin, M, m0, ncol0, N, bcol, scl);
-}
-
 // First K step of a tile: tiles running at the same time start at different K offsets, so
 // their weight streams spread over the HBM channels instead of all reading the same column
 // range of rows at a common stride.  A function of the expert and the output columns only
@@ -908,67 +660,23 @@ struct StaticSkinnyTiles {
   }
 };
 
-// One work unit: a tile of the table built in LDS.  Units from split0 on are the
-// launch's last tiles cut in two column halves (down GEMM only, see gemm_bf16_kernel):
-// unit split0 + 2 v + h is column half h of tile unit split0 + v.  Only 256- and 192-row
-// tiles are cut; of another tile, half 0 is the whole tile and half 1 is empty.
+// One tile of gemm_bf16_kernel's table: a 64-row tile (the kernel runs batches in which
+// no group is large, every group as 64-row tiles), streaming or skinny.
 template <bool GATED, bool FP8>
 __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
-                                               const int* tiles, int64_t ntile, int64_t unit,
-                                               int64_t split0) {
-  int half = -1;   // -1: the whole tile; 0 or 1: that column half
-  if (unit >= split0) {
-    const int64_t v = unit - split0;
-    unit = split0 + v / 2;
-    half = (int)(v & 1);
-  }
-  const int64_t tile = unit;
-  const int k0 = 0, nk = a.K / BK;
-  void* outp = a.out;
+                                               const int* tiles, int64_t tile) {
+  const int nk = a.K / BK;
   const int g = find_group(tiles, a.G, tile);
   int64_t row_begin;
   int M;
   group_rows(a, g, row_begin, M);
-  const bool sm = small_group<GATED>(M);
   const int narrow = a.narrow_small;
-  const int mt_g = (M + (sm ? BM_SMALL : BM_BIG) - 1) / (sm ? BM_SMALL : BM_BIG);
+  const int mt_g = (M + BM_SMALL - 1) / BM_SMALL;
   const int local = (int)(tile - tiles[g]);          // ordered (n-tile, m-tile)
   const int mt = local % mt_g;
-  const int ncol0 = (local / mt_g) * tile_cols<GATED>(sm, narrow);
-  const int rows = m_tile_rows<GATED>(M, mt);
+  const int ncol0 = (local / mt_g) * tile_cols<GATED>(true, narrow);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
-  if constexpr (!GATED) {
-    if (half >= 0) {
-      // A column half has the whole tile's K walk (rot depends on the 256-column block
-      // only), so every output element sums in the same order as in the whole tile.
-      const int nc = ncol0 + 128 * half;
-      if (nc >= a.N) return;   // a tile that holds no second half (N % 256 <= 128)
-      if (!sm && rows == BM_BIG) {
-        gemm_bf16_tile<BM_BIG / 32, 1, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, nc, k0,
-                                                   nk, rot, outp);
-        return;
-      }
-      if (!sm && rows == 192) {
-        gemm_bf16_tile<192 / 32, 1, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, nc, k0,
-                                                nk, rot, outp);
-        return;
-      }
-      if (half == 1) return;
-    }
-  }
-  if (!sm && rows == BM_BIG)
-    gemm_bf16_tile<BM_BIG / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
-                                          rot, outp);
-  else if (!sm && rows == 192)
-    gemm_bf16_tile<192 / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
-                                       rot, outp);
-  else if (!sm && rows == 128)
-    gemm_bf16_tile<128 / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0, nk,
-                                       rot, outp);
-  else if (!sm)
-    gemm_bf16_tile<BM_SMALL / 32, 2, GATED, FP8>(a, smem, g, row_begin, M, mt * BM_BIG, ncol0, k0,
-                                            nk, rot, outp);
-  else if (M - mt * BM_SMALL <= SKINNY_ROWS) {
+  if (M - mt * BM_SMALL <= SKINNY_ROWS) {
     // (gate/up takes 64-column tiles only when every group fits a skinny tile)
     const OneTile one{TileAt{g, M, mt * BM_SMALL, ncol0, rot, row_begin}};
     if (!narrow)
@@ -978,42 +686,29 @@ __device__ __forceinline__ void gemm_bf16_unit(const GemmArgs& a, bf16_t* smem,
   }
   else if (GATED || !narrow)
     gemm_bf16_tile_stream<2, GATED, STREAM_P2, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                               k0, nk, rot, outp);
+                                               0, nk, rot, a.out);
   else if constexpr (!GATED)
     gemm_bf16_tile_stream<1, GATED, STREAM_P1, FP8>(a, smem, g, row_begin, M, mt * BM_SMALL, ncol0,
-                                               k0, nk, rot, outp);
+                                               0, nk, rot, a.out);
 }
 
-// Persistent kernel over the work units in table order (group, n-tile, m-tile), dealt to
-// the 8 XCDs (blocks are dispatched to XCDs round-robin) in windows of 32 consecutive
-// units, so that the m-tiles sharing a weight tile run at the same time on one L2.
-// Down GEMM with the dynamic order: when the units leave a last round at most half full
-// (r = units mod grid, 0 < 2 r <= grid), the last r units are cut into 2 r column halves,
-// so that the last round has work for more blocks and ends about half a unit earlier.
-// Without counters block b takes unit 32 (8 r + b % 8) + b / 8 of round r (grid of 256).
-// With counters (a.ctr, 8 ints, zero at launch) each block takes its XCD's next unit
-// when it is free, so blocks that drew cheap tiles (a group's 64- or 128-row remainder)
-// take more, and an XCD that runs out helps the others.
+// Persistent kernel for batches in which no group is large (fewer tokens than the
+// small-group bound): every group as 64-row tiles, in table order (group, n-tile, m-tile),
+// dealt to the 8 XCDs (blocks are dispatched to XCDs round-robin) in windows of 32
+// consecutive units, so that the m-tiles sharing a weight tile run at the same time on one
+// L2.  Without counters block b takes unit 32 (8 r + b % 8) + b / 8 of round r (grid of
+// 256).  With counters (a.ctr, 8 ints, zero at launch) each block takes its XCD's next unit
+// when it is free, and an XCD that runs out helps the others.
 template <bool GATED, bool FP8>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
   __shared__ long long next_unit;
-  const int N = a.N, narrow = a.narrow_small;
-  auto tile_count = [N, narrow](int M) {
-    const bool sm = small_group<GATED>(M);
-    const int bm = sm ? BM_SMALL : BM_BIG, bn = tile_cols<GATED>(sm, narrow);
-    return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  };
-  build_tile_table(a, tile_count, tiles);   // ends with a barrier
-  const int64_t ntile = tiles[a.G];
-  const int64_t whole = ntile;               // work units: the tiles
-  int64_t split0 = whole;                    // first unit cut in column halves
-  if (!GATED && a.ctr != nullptr) {
-    const int64_t r = whole % gridDim.x;
-    if (r > 0 && 2 * r <= (int64_t)gridDim.x) split0 = whole - r;
-  }
-  const int64_t total = split0 + 2 * (whole - split0);
+  const int N = a.N, bn = tile_cols<GATED>(true, a.narrow_small);
+  build_tile_table(a, [N, bn](int M) {
+    return ((M + BM_SMALL - 1) / BM_SMALL) * ((N + bn - 1) / bn);
+  }, tiles);   // ends with a barrier
+  const int64_t total = tiles[a.G];
   const int x = blockIdx.x & 7;
   if (a.ctr == nullptr) {
     const int per = gridDim.x >> 3;
@@ -1028,7 +723,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       return;
     }
     for (int64_t unit = first; unit < total; unit += gridDim.x)
-      gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit, split0);
+      gemm_bf16_unit<GATED, FP8>(a, smem, tiles, unit);
     return;
   }
   for (;;) {
@@ -1050,7 +745,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int64_t unit = next_unit;
     __syncthreads();   // read by all before thread 0 writes the next one
     if (unit < 0) break;
-    gemm_bf16_unit<GATED, FP8>(a, smem, tiles, ntile, unit, split0);
+    gemm_bf16_unit<GATED, FP8>(a, smem, tiles, unit);
   }
 }
 
