@@ -11,7 +11,8 @@ against its roofline, and times the CPU oracle on a bounded sample of the same b
 The headline is the Mixtral-shaped prefill layer; with the default workload the same
 line also carries timed records of the decode, fine-grained and Switch-shaped layers
 ("workloads"), each with its layer time, tokens/s and the dominant kernel's roof
-fraction (--only: the named workload alone).
+fraction (--only: the named workload alone), and, as context for the roof fraction, the
+vendor GEMM library timed on dense products of the headline's sizes ("dense_reference").
 """
 from __future__ import annotations
 
@@ -56,6 +57,9 @@ def main():
                     help="time the named workload alone (no side workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="time only the vendor GEMM on dense products of the named workload's "
+                         "sizes (M = T k + S T kept rows, no capacity), no layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -74,12 +78,21 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dense_reference:
+        import gen
+        wl = gen.workload(args.workload)
+        cfg = {"T": wl.T, "d_model": wl.d, "d_ff": wl.F, "n_shared": wl.n_shared}
+        rec = {"config": cfg, "layer": {"kept_assignments": wl.T * wl.k}}
+        print(json.dumps({"workload": wl.name, "dense_reference": dense_reference(rec, dev)}),
+              flush=True)
+        return
     rec, inp, wl = run_workload(args.workload, args.steps, args.warmup, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = (cpu_baseline_ec if wl.routing == "expert" else cpu_baseline)(
             wl, inp, args.cpu_sample, rec["layer"]["flops"])
     del inp
     if not args.only and args.workload == "mixtral_prefill":
+        rec["dense_reference"] = dense_reference(rec, dev)
         side = {}
         for name in SIDE_WORKLOADS:
             torch.cuda.empty_cache()
@@ -308,6 +321,40 @@ def run_workload(name, steps, warmup, dev):
     del dinp, ws, out, H, Yp, calls
     return rec, inp, wl
 
+
+
+def dense_reference(rec, dev, steps=10):
+    """Context for the roof fraction: the vendor GEMM library (torch.matmul on ROCm, i.e.
+    hipBLASLt) on dense bf16 products of the headline layer's sizes, with M = the kept
+    rows (no gather, no groups, no fused SiLU*mul): [N, d] x [d, 2F] for gate/up and
+    [N, F] x [F, d] for down.  Same HIP-event timing as the stages."""
+    import torch
+
+    cfg = rec["config"]
+    n = int(rec["layer"]["kept_assignments"]) + cfg["n_shared"] * cfg["T"]
+    d, F = cfg["d_model"], cfg["d_ff"]
+    out = {"library": "torch.matmul (hipBLASLt), bf16, dense"}
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, (m, kk, nn) in (("gate_up", (n, d, 2 * F)), ("down", (n, F, d))):
+        a = torch.randn(m, kk, device=dev, dtype=torch.bfloat16, generator=g)
+        b = torch.randn(kk, nn, device=dev, dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            c = a @ b
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * m * kk * nn / (ms / 1e3) / 1e12
+        out[name] = {"shape": f"{m}x{kk}x{nn}", "ms": ms, "tflops": tf,
+                     "frac": tf / PEAK_BF16_TFLOPS}
+        log(f"[bench] dense reference {name} {m}x{kk}x{nn}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---- HBM traffic of the dominant kernel, from rocprofv3 counters
