@@ -776,10 +776,34 @@ constexpr int W8_STAGE_BF16 = 2 * W8_A_BYTES;                     // + 256 weigh
 constexpr int W8_STAGE_FP8 = W8_A_BYTES + BM_BIG * BK;            // + 256 rows of codes
 constexpr size_t W8_LDS_BYTES = 2 * W8_STAGE_BF16;                // 147456
 
+// The next unit of a block that claims its units through the per-XCD counters: the
+// counter of the block's own XCD is bumped when a tile's K loop ends, and the claim is
+// resolved (falling back to the other XCDs' counters once its own are spent) and
+// published in LDS after the tile's epilogue, so the atomic's round trip overlaps the
+// epilogue while the unit still goes to a block that is about to be free.  (Claimed when
+// the tile starts instead, a block holds its next unit a whole tile ahead: prefill down
+// 0.93 -> 0.99 ms, the last rounds lose their balance.)
+struct W8Claim {
+  long long* slot;   // LDS; nullptr: static order
+  int x;             // the block's XCD
+  int64_t total;     // units in the launch
+};
+constexpr int W8_WINDOW = 32;   // consecutive units dealt to one XCD
+__device__ inline long long w8_resolve_claim(const GemmArgs& a, const W8Claim& c, int first) {
+  int v = first;
+  for (int r = 0; r < 8; ++r) {
+    const int xr = (c.x + r) & 7;
+    if (r > 0) v = atomicAdd(&a.ctr[xr], 1);
+    const int64_t cand = ((int64_t)(v / W8_WINDOW) * 8 + xr) * W8_WINDOW + v % W8_WINDOW;
+    if (cand < c.total) return cand;
+  }
+  return -1;
+}
+
 template <int MH, int NB, bool GATED, bool FP8>
 __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
                                         int64_t row_begin, int M, int m0, int ncol0, int nk,
-                                        int rot) {
+                                        int rot, const W8Claim& claim) {
   static_assert(!GATED || NB == 2, "gate/up tiles pair the gate and up blocks in a wave");
   constexpr int STAGE = FP8 ? W8_STAGE_FP8 : W8_STAGE_BF16;      // bytes
   constexpr int NBL = FP8 ? NB : 2 * NB;   // 16-byte weight chunks per thread and step
@@ -928,6 +952,8 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
     }
   }
   if (wm == 0) __syncthreads();   // the groups' barrier counts match again
+  int claimed = 0;
+  if (claim.slot != nullptr && tid == 0) claimed = atomicAdd(&a.ctr[claim.x], 1);
 #undef W8_KSTEP
 #undef W8_LOAD_CHUNK
 #undef W8_STORE_CHUNK
@@ -981,13 +1007,15 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
         }
     }
   }
+  if (claim.slot != nullptr && tid == 0) *claim.slot = w8_resolve_claim(a, claim, claimed);
 }
 
 // One work unit of the 8-wave kernel's table: a tile, or (down GEMM, units from split0
 // on) column half v & 1 of tile split0 + v / 2, with the whole tile's K rotation.
 template <bool GATED, bool FP8>
 __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const int* tiles,
-                                        int64_t unit, int64_t split0, int nk) {
+                                        const int* offs, int64_t unit, int64_t split0, int nk,
+                                        const W8Claim& claim) {
   constexpr int COLS = GATED ? 128 : 256;   // output columns per tile
   int half = -1;
   if (!GATED && unit >= split0) {
@@ -998,7 +1026,13 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
   const int g = find_group(tiles, a.G, unit);
   int64_t row_begin;
   int M;
-  group_rows(a, g, row_begin, M);
+  if (g < a.E) {   // the dispatch offsets, copied into LDS at launch
+    row_begin = offs[g];
+    M = offs[g + 1] - offs[g];
+  } else {
+    row_begin = a.shared_row0;
+    M = a.T;
+  }
   const int bm = small_group<GATED>(M) ? BM_SMALL : BM_BIG;
   const int mt_g = (M + bm - 1) / bm;
   // A group's tiles in blocks of W8_NBLOCK n-tiles (the last block may be narrower); within
@@ -1023,18 +1057,22 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
   if constexpr (!GATED) {
     if (half >= 0) {
       const int nc = ncol0 + 128 * half;
-      if (nc >= a.N) return;   // a tile that holds no second half (N % 256 <= 128)
-      if (rows == 256) w8_tile<4, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else if (rows == 192) w8_tile<3, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else if (rows == 128) w8_tile<2, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
-      else w8_tile<1, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot);
+      if (nc >= a.N) {   // a tile that holds no second half (N % 256 <= 128)
+        if (claim.slot != nullptr && threadIdx.x == 0)
+          *claim.slot = w8_resolve_claim(a, claim, atomicAdd(&a.ctr[claim.x], 1));
+        return;
+      }
+      if (rows == 256) w8_tile<4, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot, claim);
+      else if (rows == 192) w8_tile<3, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot, claim);
+      else if (rows == 128) w8_tile<2, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot, claim);
+      else w8_tile<1, 1, false, FP8>(a, smem, g, row_begin, M, m0, nc, nk, rot, claim);
       return;
     }
   }
-  if (rows == 256) w8_tile<4, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else if (rows == 192) w8_tile<3, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else if (rows == 128) w8_tile<2, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
-  else w8_tile<1, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot);
+  if (rows == 256) w8_tile<4, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot, claim);
+  else if (rows == 192) w8_tile<3, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot, claim);
+  else if (rows == 128) w8_tile<2, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot, claim);
+  else w8_tile<1, 2, GATED, FP8>(a, smem, g, row_begin, M, m0, ncol0, nk, rot, claim);
 }
 
 // Persistent 8-wave kernel over the tile table, in the order and XCD windows of
@@ -1045,13 +1083,15 @@ template <bool GATED, bool FP8>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   __shared__ int tiles[kMaxExperts + 2];
+  __shared__ int offs[kMaxExperts + 1];
   __shared__ long long next_unit;
   constexpr int COLS = GATED ? 128 : 256;
   const int N = a.N;
+  for (int i = threadIdx.x; i <= a.E; i += blockDim.x) offs[i] = a.offsets[i];
   build_tile_table(a, [N](int M) {
     const int bm = small_group<GATED>(M) ? BM_SMALL : BM_BIG;
     return ((M + bm - 1) / bm) * ((N + COLS - 1) / COLS);
-  }, tiles);
+  }, tiles);   // ends with a barrier: offs is visible too
   const int64_t whole = tiles[a.G];
   const int nk = a.K / BK;
   int64_t split0 = whole;
@@ -1064,27 +1104,23 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   if (a.ctr == nullptr) {
     const int per = gridDim.x >> 3;
     const int64_t first = (int64_t)x * per + (blockIdx.x >> 3);
+    const W8Claim none{nullptr, x, total};
     for (int64_t unit = first; unit < total; unit += gridDim.x)
-      w8_unit<GATED, FP8>(a, smem, tiles, unit, split0, nk);
+      w8_unit<GATED, FP8>(a, smem, tiles, offs, unit, split0, nk, none);
     return;
   }
-  for (;;) {
-    if (threadIdx.x == 0) {
-      constexpr int W = 32;
-      long long u = -1;
-      for (int r = 0; r < 8 && u < 0; ++r) {
-        const int xr = (x + r) & 7;
-        const int c = atomicAdd(&a.ctr[xr], 1);
-        const int64_t cand = ((int64_t)(c / W) * 8 + xr) * W + c % W;
-        if (cand < total) u = cand;
-      }
-      next_unit = u;
-    }
+  // Units claimed through the per-XCD counters: the first here, each next one by the
+  // current unit (thread 0 writes it to next_unit at the unit's end).
+  const W8Claim claim{&next_unit, x, total};
+  if (threadIdx.x == 0) next_unit = w8_resolve_claim(a, claim, atomicAdd(&a.ctr[x], 1));
+  __syncthreads();
+  int64_t unit = next_unit;
+  __syncthreads();   // read by all before thread 0 writes the next one
+  while (unit >= 0) {
+    w8_unit<GATED, FP8>(a, smem, tiles, offs, unit, split0, nk, claim);
     __syncthreads();
-    const int64_t unit = next_unit;
-    __syncthreads();   // read by all before thread 0 writes the next one
-    if (unit < 0) break;
-    w8_unit<GATED, FP8>(a, smem, tiles, unit, split0, nk);
+    unit = next_unit;
+    __syncthreads();
   }
 }
 
