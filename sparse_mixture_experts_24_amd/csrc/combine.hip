@@ -23,9 +23,10 @@ __device__ inline void store4<bf16_t>(bf16_t* out, int64_t i, float4 v) {
   *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
 }
 
-// The slots are read KB at a time, all loads of a batch issued before any is used (a
-// dropped slot loads row 0 and contributes nothing), so each thread keeps KB 16-byte loads
-// in flight; the sum runs over the slots in ascending order.
+// The slots are read KB at a time (KB = 8 for k > 4: the fine-grained layer's 8 slots and
+// its shared row in one batch), all loads of a batch issued before any is used (a dropped
+// slot loads row 0 and contributes nothing), so each thread keeps up to KB + 1 16-byte
+// loads in flight; the sum runs over the slots in ascending order, the shared row last.
 template <typename OutT, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp,
                                                       const int32_t* __restrict__ slot_pos,
@@ -42,6 +43,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t srow = (int64_t)T * k + t;
   for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    // the shared expert's row is loaded with the first batch of slots, added after all
+    float4 vs = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (shared) vs = *reinterpret_cast<const float4*>(Yp + srow * d + c);
     for (int j0 = 0; j0 < k; j0 += KB) {
       float4 v[KB];
       bool ok[KB];
@@ -64,11 +68,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
     if (shared) {
-      const float4 v = *reinterpret_cast<const float4*>(Yp + srow * d + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      acc.x += vs.x;
+      acc.y += vs.y;
+      acc.z += vs.z;
+      acc.w += vs.w;
     }
     store4<OutT>(out, (int64_t)t * d + c, acc);
   }
@@ -85,8 +88,11 @@ static void launch_combine_o(const moe_desc_t& d, const float* Yp, const int32_t
   else if (k == 2)
     hipLaunchKernelGGL((combine_kernel<OutT, 2>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
                        dm, sh, out);
-  else
+  else if (k <= 4)
     hipLaunchKernelGGL((combine_kernel<OutT, 4>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
+                       dm, sh, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<OutT, 8>), grid, block, 0, s, Yp, slot_pos, topk_w, T, k,
                        dm, sh, out);
 }
 
