@@ -823,11 +823,13 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
     const int m = m0 + lr + 64 * i;
     aoff[i] = m < M ? m : 0;
   }
-  if (GATED && g < a.E) {
+  // Routed gate/up rows: the slot indices are loaded here and turned into token-row
+  // offsets in the prologue, after the weight rows of step 0 are requested (those do not
+  // depend on them), so the two round trips overlap.
+  const bool gathered = GATED && g < a.E;
+  if (gathered) {
 #pragma unroll
     for (int i = 0; i < MH; ++i) aoff[i] = a.perm_src[row_begin + aoff[i]];
-#pragma unroll
-    for (int i = 0; i < MH; ++i) aoff[i] = aoff[i] / a.topk * K + lc;
   } else {
     const int base = GATED ? 0 : (int)row_begin;     // shared expert: token m; down: row
 #pragma unroll
@@ -913,14 +915,35 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
 
   // Prologue: step 0 in stage 0, steps 1 .. PF in the register sets.
+  if constexpr (GATED) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) W8_LOAD_CHUNK(0, i, 0);
+    for (int i = MH; i < NCH; ++i) W8_LOAD_CHUNK(0, i, 0);   // weight rows of step 0
+    __builtin_amdgcn_sched_barrier(0);
+    if (gathered) {
+#pragma unroll
+      for (int i = 0; i < MH; ++i) aoff[i] = aoff[i] / a.topk * K + lc;
+    }
+#pragma unroll
+    for (int i = 0; i < MH; ++i) W8_LOAD_CHUNK(0, i, 0);      // token rows of step 0
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) W8_LOAD_CHUNK(0, i, 0);
+  }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) W8_STORE_CHUNK(0, i, 0);
+  // Steps 1 .. PF in the loop's own order (gate/up: pinned by scheduling barriers): the
+  // vector-memory counter retires loads in issue order, and the counts the compiler waits
+  // for at the top of the K loop must also hold on entry, or every step waits for loads
+  // issued one phase earlier.  (The down GEMM's loop already waits exactly; pinned there
+  // too, it ran ~1% slower.)
+  if constexpr (GATED) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 1; q <= PF; ++q)
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) W8_LOAD_CHUNK(q % PF, i, q);
+    for (int i = 0; i < NCH; ++i) {
+      W8_LOAD_CHUNK(q % PF, i, q);
+      if constexpr (GATED) __builtin_amdgcn_sched_barrier(0);
+    }
   __syncthreads();
   if (wm == 1) __syncthreads();   // group 1 runs one phase behind
   for (int t0 = 0; t0 < nk; t0 += PF) {
