@@ -934,8 +934,9 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
   // Steps 1 .. PF in the loop's own order (gate/up: pinned by scheduling barriers): the
   // vector-memory counter retires loads in issue order, and the counts the compiler waits
   // for at the top of the K loop must also hold on entry, or every step waits for loads
-  // issued one phase earlier.  (The down GEMM's loop already waits exactly; pinned there
-  // too, it ran ~1% slower.)
+  // issued one phase earlier.  (The down GEMM is left as it was: its 256-row loop already
+  // waits exactly, and with the pinning and the loop shape below, for all of its tiles or
+  // only the 64-192-row ones, the prefill down GEMM ran 1-3% slower.)
   if constexpr (GATED) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 1; q <= PF; ++q)
@@ -973,8 +974,7 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
   if constexpr (GATED) {
     // Whole groups of PF steps in the loop, the last nk % PF after it: a loop body left
     // early joins the loop head with a partial group's loads in flight, and the compiler
-    // then waits at every step as if the last-issued set came first.  (The down GEMM keeps
-    // the early exit: restructured the same way it ran 2-3% slower, its waits unchanged.)
+    // then waits at every step as if the last-issued set came first.
     int t0 = 0;
     for (; t0 + PF <= nk; t0 += PF) {
 #pragma unroll
