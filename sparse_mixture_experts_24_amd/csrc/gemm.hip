@@ -157,14 +157,15 @@ template <bool GATED>
 __device__ inline bool small_group(int M) {
   return M < (GATED ? SMALL_GROUP_ROWS_GATED : SMALL_GROUP_ROWS_DOWN);
 }
-// Rows of m-tile mt (tiles start at mt * 256 in large groups, mt * 64 in small ones):
-// large groups take 256-row tiles and put their remainder in one tile of 64, 128, 192 or
-// 256 rows, whichever is the smallest that holds it.
+// Rows of m-tile mt (tiles start at mt * B in large groups, mt * 64 in small ones): large
+// groups are cut into tiles of B rows (256, or 192 for down GEMMs whose rounds that fills
+// better, see down_tile_rows) and put their remainder in one tile of 64, 128, 192 or B
+// rows, whichever is the smallest that holds it.
 template <bool GATED>
-__device__ inline int m_tile_rows(int M, int mt) {
+__device__ inline int m_tile_rows(int M, int mt, int B) {
   if (small_group<GATED>(M)) return BM_SMALL;
-  const int r = M - mt * BM_BIG;
-  return r > 192 ? BM_BIG : r > 128 ? 192 : r > 64 ? 128 : 64;
+  const int r = M - mt * B;
+  return r > 192 ? B : r > 128 ? 192 : r > 64 ? 128 : 64;
 }
 template <bool GATED>
 __device__ inline int tile_cols(bool small, int narrow_small) {
@@ -776,6 +777,66 @@ constexpr int W8_STAGE_BF16 = 2 * W8_A_BYTES;                     // + 256 weigh
 constexpr int W8_STAGE_FP8 = W8_A_BYTES + BM_BIG * BK;            // + 256 rows of codes
 constexpr size_t W8_LDS_BYTES = 2 * W8_STAGE_BF16;                // 147456
 
+// Row height of the down GEMM's large tiles, 256 or 192, chosen per launch from the
+// dispatch offsets (every block computes the same value).  Estimated time of a launch:
+// rounds x mean unit cost, where a unit of r rows costs 31 + r (the 256-row tile's K loop
+// took 1/0.777 of the 192-row one's per launch on the Mixtral-shaped prefill layer) and
+// the rounds n / grid are rounded up to the next half (the last round's column halves,
+// dynamic order) or whole.  Few rounds: the quantisation decides (Mixtral-shaped prefill,
+// 576 units = 2.25 rounds of 256-row tiles against 768 = 3 of 192-row ones: down 0.946 ->
+// 0.882 ms; Switch-shaped 0.524 -> 0.515); many rounds: the padded work decides
+// (fine-grained layer: 256, where 192 ran 3.5% slower).  The summation order does not
+// depend on the tile shape, so neither do the results.  Wave 0; ends with a barrier.
+__device__ inline int down_tile_rows(const GemmArgs& a, const int* offs, bool halves,
+                                     int* out) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int64_t NT = (a.N + 255) / 256;
+    long long n[2] = {0, 0}, w[2] = {0, 0};
+    for (int base = 0; base < a.G; base += 64) {
+      const int g = base + lane;
+      const int M = g < a.G ? (g < a.E ? offs[g + 1] - offs[g] : a.T) : 0;
+      if (M > 0) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int B = v == 0 ? 256 : 192;
+          if (small_group<false>(M)) {
+            const int mt = (M + BM_SMALL - 1) / BM_SMALL;
+            n[v] += mt * NT;
+            w[v] += mt * NT * (31 + BM_SMALL);
+          } else {
+            const int mt = (M + B - 1) / B;
+            n[v] += mt * NT;
+            w[v] += NT * ((mt - 1) * (31 + B) + 31 + m_tile_rows<false>(M, mt - 1, B));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      for (int o = 32; o > 0; o >>= 1) {
+        n[v] += __shfl_xor(n[v], o, 64);
+        w[v] += __shfl_xor(w[v], o, 64);
+      }
+    if (lane == 0) {
+      double est[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if (n[v] == 0) {
+          est[v] = 0.0;
+          continue;
+        }
+        const double R = (double)n[v] / (double)gridDim.x, fl = floor(R), fr = R - fl;
+        const double rounds = fr == 0.0 ? fl : (halves && fr <= 0.5) ? fl + 0.5 : fl + 1.0;
+        est[v] = rounds * (double)w[v] / (double)n[v];
+      }
+      *out = est[1] < 0.98 * est[0] ? 192 : 256;
+    }
+  }
+  __syncthreads();
+  return *out;
+}
+
 // The next unit of a block that claims its units through the per-XCD counters: the
 // counter of the block's own XCD is bumped when a tile's K loop ends, and the claim is
 // resolved (falling back to the other XCDs' counters once its own are spent) and
@@ -1057,8 +1118,8 @@ __device__ __forceinline__ void w8_tile(const GemmArgs& a, bf16_t* smem, int g,
 // on) column half v & 1 of tile split0 + v / 2, with the whole tile's K rotation.
 template <bool GATED, bool FP8>
 __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const int* tiles,
-                                        const int* offs, int64_t unit, int64_t split0, int nk,
-                                        const W8Claim& claim) {
+                                        const int* offs, int bmb, int64_t unit, int64_t split0,
+                                        int nk, const W8Claim& claim) {
   constexpr int COLS = GATED ? 128 : 256;   // output columns per tile
   int half = -1;
   if (!GATED && unit >= split0) {
@@ -1076,7 +1137,7 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
     row_begin = a.shared_row0;
     M = a.T;
   }
-  const int bm = small_group<GATED>(M) ? BM_SMALL : BM_BIG;
+  const int bm = small_group<GATED>(M) ? BM_SMALL : bmb;
   const int mt_g = (M + bm - 1) / bm;
   // A group's tiles in blocks of W8_NBLOCK n-tiles (the last block may be narrower); within
   // a block m-tile major, so a window of 32 consecutive units is 8 m-tiles x 4 n-tiles
@@ -1094,7 +1155,7 @@ __device__ __forceinline__ void w8_unit(const GemmArgs& a, bf16_t* smem, const i
     nt = full * W8_NBLOCK + rem % wd;
   }
   const int ncol0 = nt * COLS;
-  const int rows = m_tile_rows<GATED>(M, mt);
+  const int rows = m_tile_rows<GATED>(M, mt, bmb);
   const int rot = k_rotation<GATED>(g, ncol0, nk);
   const int m0 = mt * bm;
   if constexpr (!GATED) {
@@ -1130,9 +1191,15 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   __shared__ long long next_unit;
   constexpr int COLS = GATED ? 128 : 256;
   const int N = a.N;
+  __shared__ int bmb_s;
   for (int i = threadIdx.x; i <= a.E; i += blockDim.x) offs[i] = a.offsets[i];
-  build_tile_table(a, [N](int M) {
-    const int bm = small_group<GATED>(M) ? BM_SMALL : BM_BIG;
+  int bmb = BM_BIG;
+  if constexpr (!GATED) {
+    __syncthreads();
+    bmb = down_tile_rows(a, offs, a.ctr != nullptr, &bmb_s);
+  }
+  build_tile_table(a, [N, bmb](int M) {
+    const int bm = small_group<GATED>(M) ? BM_SMALL : bmb;
     return ((M + bm - 1) / bm) * ((N + COLS - 1) / COLS);
   }, tiles);   // ends with a barrier: offs is visible too
   const int64_t whole = tiles[a.G];
@@ -1149,7 +1216,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
     const int64_t first = (int64_t)x * per + (blockIdx.x >> 3);
     const W8Claim none{nullptr, x, total};
     for (int64_t unit = first; unit < total; unit += gridDim.x)
-      w8_unit<GATED, FP8>(a, smem, tiles, offs, unit, split0, nk, none);
+      w8_unit<GATED, FP8>(a, smem, tiles, offs, bmb, unit, split0, nk, none);
     return;
   }
   // Units claimed through the per-XCD counters: the first here, each next one by the
@@ -1160,7 +1227,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   int64_t unit = next_unit;
   __syncthreads();   // read by all before thread 0 writes the next one
   while (unit >= 0) {
-    w8_unit<GATED, FP8>(a, smem, tiles, offs, unit, split0, nk, claim);
+    w8_unit<GATED, FP8>(a, smem, tiles, offs, bmb, unit, split0, nk, claim);
     __syncthreads();
     unit = next_unit;
     __syncthreads();
