@@ -250,8 +250,9 @@ def test_batch_consistency(name):
     """Without a capacity, a token's output does not depend on the rest of the batch:
     batches of 1, 32 and 64 give bit-identical rows ("Mixture-of-experts in practice",
     inference-stability section, batch-consistency check).  The larger cases run the
-    full batch with 256-row tiles, the dynamic tile order and the down GEMM's column
-    halves, the sub-batches with 64-row and skinny tiles."""
+    full batch with 256-row tiles (the down GEMM with 192-row ones where they fill its
+    rounds better), the dynamic tile order and the down GEMM's column halves, the
+    sub-batches with 64-row and skinny tiles."""
     wl = CASES[name]
     inp = to_dev(gen.make_inputs(wl), DEV)
     args = (inp["router_bias"], inp["W_gate"], inp["W_up"], inp["W_down"], wl.k, 0.0)
